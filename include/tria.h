@@ -1,0 +1,151 @@
+/*
+ * tria.h -- C ABI of the TriAttention KV-cache prune step on AMD MI355X (gfx950).
+ *
+ * The prune step, per stream (one sequence s, one layer l, one KV head g) of N cached keys:
+ *   1. score every cached key for each of the G query heads that share the KV head with the
+ *      trigonometric-series score plus the (1-R)-weighted norm score, future offsets averaged;
+ *   2. z-score each query head's scores over the stream and take the max over the GQA group;
+ *   3. keep the top B keys (ties to the lower index), in ascending index order;
+ *   4. compact K, V and the key positions in place.
+ * Definitions follow the pages on "TriAttention: Efficient Long Reasoning with Trigonometric KV
+ * Compression" (arXiv 2604.04921):
+ *   - scores: zhichai.net, "旋转舞台上的追光者..." section "TriAttention：把理论变成算法" items 1-2;
+ *     chenxutan.com/d/2624, "TriAttention深度解析..." sections 3.1-3.3 (trig series, offsets D);
+ *   - (1-R) weight, sum of the two parts, GQA z-score + max, 128-token cadence:
+ *     10100.com/article/127765992 section "TriAttention方法"; watermelonwater.tech,
+ *     "TriAttention：面向长文本推理的高效KV缓存压缩..." section "TriAttention 方案设计" item 4;
+ *   - top-B kept in original order: chenxutan.com/d/2624 section 4.2 (prune_kv_cache).
+ *
+ * Conventions shared by every call:
+ *   - head_dim d = 128.  A d-vector is read in the half-split RoPE layout: band f (f < 64) is
+ *     the complex number v[f] + i*v[f+64].  w_f = fl32(theta^(-2f/d)) (fp64 power, rounded once).
+ *   - Cached keys are post-RoPE: band f of key j holds k_f * exp(i*w_f*p_j).
+ *   - A stream's id is (s*L + l)*Hkv + g; query head h belongs to KV head h / G, G = Hq/Hkv.
+ *   - Device buffers are plain device pointers allocated and owned by the caller.  Layouts:
+ *       K, V    [S][L][Hkv][N][128]   dtype bf16 or fp32, rows contiguous
+ *       pos     [S][L][Hkv][N]        int32
+ *       t       [S]                   int32, position of the newest cached token
+ *       F       [S][L][Hkv][N]        fp32 final scores
+ *       kept    [S][L][Hkv][min(B,N)] int32, ascending
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call is
+ *     asynchronous on that stream; host-detectable argument errors return before any launch.
+ *   - No call allocates device memory except tria_load_calib (the calibration table).  Scratch
+ *     space is a caller-owned workspace sized by the *_workspace_bytes functions.
+ *   - Errors are returned as tria_status; nothing is thrown across the ABI.
+ */
+#ifndef TRIA_H
+#define TRIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TRIA_OK = 0,
+    TRIA_E_INVALID = -1,      /* bad argument: null pointer, bad size, misaligned buffer */
+    TRIA_E_UNSUPPORTED = -2,  /* valid but not implemented: head_dim != 128, G > 8, ... */
+    TRIA_E_NOMEM = -3,        /* device allocation failed (tria_load_calib only) */
+    TRIA_E_DEVICE = -4,       /* a HIP runtime call or kernel launch failed */
+    TRIA_E_NONFINITE = -5,    /* a non-finite key value or score was met (see tria_score_check) */
+    TRIA_E_WORKSPACE = -6     /* workspace pointer missing or smaller than required */
+} tria_status;
+
+typedef enum { TRIA_BF16 = 0, TRIA_F32 = 1 } tria_dtype;
+
+/* tria_score flags */
+#define TRIA_PER_KEY_PHASE 1u /* recover each key's pre-RoPE band phase from its position
+                                 (exact integer range reduction of w_f*p) and evaluate the score
+                                 in the literal per-key form; same result, more arithmetic. */
+#define TRIA_KEYS_PRE_ROPE 2u /* keys are stored before RoPE (k_f, not k_f*exp(i w_f p)); the
+                                 score then needs each key's distance phase w_f*(t-p_j). */
+
+typedef struct tria_calib tria_calib; /* opaque, library-owned, immutable after load */
+
+/*
+ * Build the calibration table from offline statistics (chenxutan.com/d/2624 section 3.4;
+ * zhichai.net section "破局之道" for R; watermelonwater.tech "TriAttention 方案设计" item 1).
+ *   q_centre    host [L][Hq][d]   pre-RoPE query centres qbar (half-split layout)
+ *   q_band_norm host [L][Hq][d/2] E|q_f| >= 0
+ *   r_band      host [L][Hq][d/2] R_f in [0, 1]
+ *   rope_theta  RoPE base (> 1)
+ *   offsets     host [n_offsets]  future offsets D (each in [0, 2^24)); NULL with
+ *               n_offsets = 0 selects D = {1, 2, 4, ..., 2^16}
+ * The table holds, per (layer, query head), qbar_f * mean_d exp(i w_f d) and the norm weights
+ * (1 - R_f) E|q_f|, plus w_f / 2pi per band as a 64-bit fixed-point fraction of a turn.
+ * Host arrays are read during the call only.  The table is uploaded with a synchronous copy
+ * ordered after `stream`.  *out receives a handle freed with tria_free_calib.
+ * Errors: INVALID (null/negative/non-finite/out-of-range input), UNSUPPORTED (head_dim != 128,
+ * Hq not a multiple of Hkv, G > 8), NOMEM, DEVICE.
+ */
+tria_status tria_load_calib(tria_calib **out, int n_layers, int n_q_heads, int n_kv_heads,
+                            int head_dim, const float *q_centre, const float *q_band_norm,
+                            const float *r_band, double rope_theta, const int32_t *offsets,
+                            int n_offsets, void *stream);
+void tria_free_calib(tria_calib *calib);
+
+/* Shape queries of a loaded table (return -1 for a NULL handle). */
+int tria_calib_dim(const tria_calib *calib, int which /* 0 L, 1 Hq, 2 Hkv, 3 d, 4 G */);
+
+/* Workspace bytes tria_score needs for n_seq sequences of n_keys keys (0 on bad arguments). */
+size_t tria_score_workspace_bytes(const tria_calib *calib, int n_seq, int n_keys);
+
+/*
+ * Score every key of every stream and write the final score F (steps 1-2 above).
+ *   k          device [S][L][Hkv][N][128] keys (dtype), 16-byte aligned
+ *   pos        device [S][L][Hkv][N] key positions (read only with TRIA_PER_KEY_PHASE or
+ *              TRIA_KEYS_PRE_ROPE; may be NULL otherwise)
+ *   t          device [S] current positions
+ *   F          device [S][L][Hkv][N] output final scores
+ *   raw        device [S][L][Hq][N] optional output of the raw scores S_trig + S_norm (NULL: not written)
+ *   head_stats device [S][L][Hq][2] optional output of each head's (mean, population std)
+ *   ws         device workspace of at least tria_score_workspace_bytes(), 256-byte aligned;
+ *              its contents need not be initialised.
+ * Positions and t must satisfy |t - p| < 2^24 and |t + d| < 2^31.
+ * A head whose raw scores span at most 2^-16 of their largest magnitude (equal up to rounding)
+ * is constant: std 0, and it contributes z = 0.
+ * Non-finite raw scores set a flag in the workspace; read it with tria_score_check.
+ */
+tria_status tria_score(const tria_calib *calib, tria_dtype dtype, const void *k, const int32_t *pos,
+                       const int32_t *t, int n_seq, int n_keys, float *F, float *raw,
+                       float *head_stats, unsigned flags, void *ws, size_t ws_bytes, void *stream);
+
+/* Synchronise `stream` and report TRIA_E_NONFINITE if the last tria_score on this workspace
+ * met a non-finite score, else TRIA_OK (TRIA_E_DEVICE on a runtime error). */
+tria_status tria_score_check(const void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes tria_select_topB needs (0 on bad arguments). */
+size_t tria_select_workspace_bytes(int n_streams, int n_keys, int budget);
+
+/*
+ * Top-B selection per stream (step 3): kept[s][0..min(B,N)) = the indices of the min(B,N)
+ * largest F, ties to the lower index, -0 equal to +0, written in ascending order.
+ * B >= N gives kept = 0..N-1.  F must be finite (guaranteed when tria_score_check is OK).
+ *   F    device [n_streams][N] fp32;  kept device [n_streams][min(B,N)] int32.
+ */
+tria_status tria_select_topB(const float *F, int n_streams, int n_keys, int budget, int32_t *kept,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * In-place, order-preserving compaction (step 4): for i < min(B,N), row i of K, V and pos takes
+ * row kept[i].  kept must be strictly ascending with kept[i] in [i, N) (as tria_select_topB
+ * writes it).  Rows >= min(B,N) are left as they were.  k, v 16-byte aligned; pos may be NULL.
+ */
+tria_status tria_compact(tria_dtype dtype, void *k, void *v, int32_t *pos, const int32_t *kept,
+                         int n_streams, int n_keys, int budget, int head_dim, void *stream);
+
+/* Whole prune step: tria_score, tria_select_topB and tria_compact in sequence on `stream`,
+ * with kept written to the caller's buffer.  ws must hold tria_prune_workspace_bytes(). */
+size_t tria_prune_workspace_bytes(const tria_calib *calib, int n_seq, int n_keys, int budget);
+tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void *v, int32_t *pos,
+                       const int32_t *t, int n_seq, int n_keys, int budget, float *F,
+                       int32_t *kept, unsigned flags, void *ws, size_t ws_bytes, void *stream);
+
+const char *tria_status_string(tria_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRIA_H */

@@ -1,0 +1,58 @@
+// tria_internal.h -- private declarations shared by the host ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tria.h"
+
+#define TRIA_D 128      // head_dim
+#define TRIA_HALF 64    // RoPE bands per head
+#define TRIA_MAX_G 8    // largest GQA group handled
+
+struct tria_calib {
+    int L, Hq, Hkv, d, G;
+    double theta;
+    int n_off;
+    int device;
+    // device table (one allocation, `block`)
+    void *block;
+    size_t block_bytes;
+    double2 *P;      // [L][Hq][64] qbar_f * mean_{d in D} exp(i w_f d)   (fp64)
+    float2 *P32;     // [L][Hq][64] the same rounded to fp32
+    float *W;        // [L][Hq][64] norm weights (1 - R_f) E|q_f|
+    uint64_t *nu;    // [64] w_f / (2 pi) as a 64-bit fraction of a turn
+};
+
+// Workspace layout of tria_score (every region 256-byte aligned).
+struct tria_score_ws {
+    size_t qrot_off, raw_off, part_off, err_off, total;
+    int tiled;       // 1: raw scores round-trip through the workspace (large streams)
+    int tiles;       // key tiles per stream on the tiled path
+};
+
+namespace tria {
+
+constexpr int kTileKeys = 1024;       // keys per block on the tiled scoring path
+constexpr int kScoreThreads = 256;
+constexpr int kFusedLdsMax = 80 * 1024;   // raw scores of a stream kept on chip up to this size
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectLdsKeys = 36864;     // streams up to this many keys are selected from LDS
+constexpr int kCompactThreads = 256;
+constexpr int kCompactRows = 64;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+tria_score_ws score_ws_layout(const tria_calib *c, int n_seq, int n_keys);
+
+// kernel launchers (return hipSuccess or the launch error)
+hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, hipStream_t st);
+hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
+                        const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
+                        float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st);
+hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st);
+hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
+                          int n_streams, int N, int B, hipStream_t st);
+
+}  // namespace tria

@@ -31,7 +31,10 @@
  *  - Per query head: z = (s - mean)/std over the N keys of the stream (population std); the
  *    final key score is the max of z over the G query heads of the GQA group
  *    ([p4] "TriAttention方法" last paragraph; [p5] "TriAttention 方案设计" item 4).
- *    If every raw score of a head is identical the std is zero and z := 0 for that head.
+ *    The pages do not say what a head whose scores are all equal contributes; such a head
+ *    carries no ranking information, so its z is 0.  Scores that are mathematically equal
+ *    differ by rounding, so a head whose scores span at most 2^-16 of their largest magnitude
+ *    counts as constant (std reported as 0, z := 0).
  *  - Keep the top B keys by (final score descending, index ascending), output ascending
  *    ([p1] section 4.2, prune_kv_cache: topk then sort to keep the order).
  *  - Compaction: row i of K, V and positions takes row kept[i], i < min(B, N).
@@ -156,8 +159,9 @@ void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const
 /*
  * z-score per head and max over the G heads.
  *   raw [G][N] -> z [G][N] (may be NULL), F [N], mu [G], sd [G] (may be NULL).
- * Population mean and std over the N keys.  A head whose raw scores are all identical has
- * std 0 and z = 0.  Returns 0, or -1 if any raw score is not finite.
+ * Population mean and std over the N keys.  A head whose raw scores span at most 2^-16 of
+ * their largest magnitude is constant: std 0 and z = 0.  Returns 0, or -1 if any raw score is
+ * not finite.
  */
 int oracle_zmax(int N, int G, const double *raw, double *z, double *F, double *mu, double *sd)
 {
@@ -174,7 +178,9 @@ int oracle_zmax(int N, int G, const double *raw, double *z, double *F, double *m
         double m = sum / N;
         double var = 0.0;
         for (int j = 0; j < N; ++j) var += (s[j] - m) * (s[j] - m);
-        double sig = (lo == hi) ? 0.0 : sqrt(var / N);
+        double big = fabs(lo) > fabs(hi) ? fabs(lo) : fabs(hi);
+        int constant = (hi - lo) <= ldexp(big, -16);
+        double sig = constant ? 0.0 : sqrt(var / N);
         if (mu) mu[h] = m;
         if (sd) sd[h] = sig;
         for (int j = 0; j < N; ++j) {

@@ -260,3 +260,31 @@ def algorithmic_bytes(cfg: Config, moved_rows: int | None = None) -> int:
     N = cfg.n_keys
     M = min(cfg.budget, N) * cfg.n_streams if moved_rows is None else moved_rows
     return cfg.n_streams * (N * r + 8 * N) + M * (4 * r + 8)
+
+
+def to_device(wl: dict, device="cuda") -> dict:
+    """Upload a host workload (``make_host``) to device tensors (same keys, torch tensors)."""
+    import torch
+
+    cfg = wl["cfg"]
+
+    def cache(a):
+        if cfg.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    out = dict(wl)
+    out["k"] = cache(wl["k"])
+    out["v"] = cache(wl["v"])
+    out["pos"] = torch.from_numpy(np.ascontiguousarray(wl["pos"])).to(device)
+    out["t_dev"] = torch.from_numpy(np.ascontiguousarray(wl["t"], dtype=np.int32)).to(device)
+    return out
+
+
+def cache_to_host(x) -> np.ndarray:
+    """Device cache tensor -> numpy (float32, or uint16 bf16 bit patterns)."""
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).cpu().numpy().view(np.uint16)
+    return x.cpu().numpy()

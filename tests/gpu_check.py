@@ -1,0 +1,106 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and compare it with the
+fp64 oracle on the same seeded inputs.
+
+Tolerances (fp32 accumulation against fp64):
+  raw scores   |s_gpu - s_orc| <= 1e-4 * max(|s_orc|, std_h)      (std_h: the head's oracle std)
+  final score  |F_gpu - F_orc| <= 1e-4 * max(|F_orc|, 1)
+  kept sets    identical except keys whose oracle score lies within 1e-4 * max(1, |F_B|) of the
+               oracle's B-th largest score F_B
+  selection    bit-exact against the oracle's selection run on the GPU's own final scores
+  compaction   bit-exact against fancy indexing of a pristine copy
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+
+RAW_RTOL = 1e-4
+F_RTOL = 1e-4
+
+
+def gpu_prune(T, calib, dev, budget, want_raw=True, flags=0):
+    """Score, select and compact through the C ABI; returns host copies of everything."""
+    import torch
+
+    k, v, pos, t = dev["k"], dev["v"], dev["pos"], dev["t_dev"]
+    S, L, Hkv, N, d = k.shape
+    Hq = calib.n_q_heads
+    raw = torch.empty((S, L, Hq, N), dtype=torch.float32, device=k.device) if want_raw else None
+    stats = torch.empty((S, L, Hq, 2), dtype=torch.float32, device=k.device)
+    ws = T.workspace(T.score_workspace_bytes(calib, S, N), k.device)
+    F = T.score(calib, k, t, raw=raw, head_stats=stats, pos=pos, flags=flags, ws=ws)
+    T.score_check(ws)
+    kept = T.select_topB(F, budget)
+    T.compact(k, v, pos, kept, budget)
+    torch.cuda.synchronize()
+    out = {"F": F.cpu().numpy().reshape(-1, N), "kept": kept.cpu().numpy(),
+           "stats": stats.cpu().numpy().reshape(-1, calib.G, 2)}
+    if want_raw:
+        out["raw"] = raw.cpu().numpy().reshape(-1, calib.G, N)
+    return out
+
+
+def oracle_prune(orc, wl_host_streams, pos_streams, t, qc, qn, rb, budget, Hkv, ids, form):
+    return orc.prune_streams(wl_host_streams, pos_streams, t, qc, qn, rb, budget, Hkv, stream_ids=ids,
+                             form=form, want_raw=True)
+
+
+def check_raw(raw_gpu, raw_orc):
+    """raw_* [n][G][N]."""
+    sd = raw_orc.std(axis=2, keepdims=True)
+    scale = np.maximum(np.abs(raw_orc), sd)
+    err = np.abs(raw_gpu.astype(np.float64) - raw_orc) / scale
+    assert np.all(np.isfinite(raw_gpu))
+    worst = float(err.max())
+    assert worst <= RAW_RTOL, f"raw score relative error {worst:.3g} > {RAW_RTOL}"
+    return worst
+
+
+def check_F(F_gpu, F_orc):
+    err = np.abs(F_gpu.astype(np.float64) - F_orc) / np.maximum(np.abs(F_orc), 1.0)
+    worst = float(err.max())
+    assert worst <= F_RTOL, f"final score relative error {worst:.3g} > {F_RTOL}"
+    return worst
+
+
+def check_kept_sets(kept_gpu, kept_orc, F_orc, budget):
+    """Sets may differ only on near-threshold keys (by the oracle's scores)."""
+    n, N = F_orc.shape
+    n_diff = 0
+    for i in range(n):
+        a, b = set(kept_gpu[i].tolist()), set(kept_orc[i].tolist())
+        if a == b:
+            continue
+        nk = min(budget, N)
+        FB = np.sort(F_orc[i])[::-1][nk - 1]
+        tol = 1e-4 * max(1.0, abs(FB))
+        for j in a ^ b:
+            assert abs(F_orc[i, j] - FB) <= tol, f"stream {i}: key {j} differs and is not near the threshold"
+        n_diff += 1
+    return n_diff
+
+
+def check_select_exact(orc, kept_gpu, F_gpu, budget):
+    for i in range(F_gpu.shape[0]):
+        ref = orc.select(F_gpu[i].astype(np.float64), budget)
+        assert np.array_equal(kept_gpu[i], ref), f"stream {i}: selection differs from a full sort"
+
+
+def check_compaction(before, after, kept, budget):
+    """before/after [n][N][...] host arrays of one tensor; kept [n][nk]."""
+    n, N = before.shape[0], before.shape[1]
+    nk = min(budget, N)
+    for i in range(n):
+        exp = before[i][kept[i]]
+        assert np.array_equal(after[i][:nk], exp), f"stream {i}: compacted rows differ"
+        assert np.array_equal(after[i][nk:], before[i][nk:]), f"stream {i}: rows past B were touched"
+
+
+def streams_of(x, N):
+    """[S][L][Hkv][N][...] -> [streams][N][...]"""
+    return x.reshape((-1, N) + x.shape[4:])
+
+
+def host_cache(x):
+    return synth.cache_to_host(x)

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle (run on an MI355X).
+
+Covers the small configurations in full, group sizes 1..8, both scoring paths (raw scores kept
+on chip, and the tiled path with a ragged last tile), fp32 and bf16 caches, and the degenerate
+cases (one key, B >= N, constant streams, ties, non-finite keys).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from tests import gpu_check as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_compression_tria_amd as T
+    T.lib()
+    return T
+
+
+def variant(base: int, **kw):
+    return dataclasses.replace(synth.CONFIGS[base], **kw)
+
+
+def run_case(orc, T, cfg, form="fac", sample=None, flags=0):
+    print(f"\n[case] {cfg.describe()} form={form} flags={flags}", flush=True)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    N, B = cfg.n_keys, cfg.budget
+    kb, vb, pb = gc.streams_of(wl["k"], N), gc.streams_of(wl["v"], N), gc.streams_of(wl["pos"], N)
+    out = gc.gpu_prune(T, calib, dev, B, flags=flags)
+    ids = np.arange(cfg.n_streams) if sample is None else np.asarray(sample)
+    res = orc.prune_streams(kb[ids], pb[ids], wl["t"], wl["qc"], wl["qn"], wl["rb"], B, cfg.n_kv_heads,
+                            stream_ids=ids, form=form, want_raw=True)
+    e_raw = gc.check_raw(out["raw"][ids], res["raw"])
+    e_F = gc.check_F(out["F"][ids], res["F"])
+    n_diff = gc.check_kept_sets(out["kept"][ids], res["kept"], res["F"], B)
+    gc.check_select_exact(orc, out["kept"][ids], out["F"][ids], B)
+    mu = res["raw"].mean(axis=2)
+    sd = res["raw"].std(axis=2)
+    np.testing.assert_allclose(out["stats"][ids, :, 0], mu, rtol=1e-5, atol=1e-5 * np.abs(sd).max())
+    np.testing.assert_allclose(out["stats"][ids, :, 1], sd, rtol=1e-4)
+    ka = gc.streams_of(gc.host_cache(dev["k"]), N)
+    va = gc.streams_of(gc.host_cache(dev["v"]), N)
+    pa = gc.streams_of(dev["pos"].cpu().numpy(), N)
+    gc.check_compaction(kb[ids], ka[ids], out["kept"][ids], B)
+    gc.check_compaction(vb[ids], va[ids], out["kept"][ids], B)
+    gc.check_compaction(pb[ids], pa[ids], out["kept"][ids], B)
+    print(f"[ok] raw err {e_raw:.2e}  F err {e_F:.2e}  streams with near-threshold set differences {n_diff}",
+          flush=True)
+    calib.free()
+    return out, res
+
+
+def test_config1_tiny_fp32_literal_oracle(orc, T):
+    run_case(orc, T, synth.CONFIGS[1], form="lit")
+
+
+def test_config2_qwen3_8b_layer_literal_oracle(orc, T):
+    run_case(orc, T, synth.CONFIGS[2], form="lit")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 6, 7, 8])
+def test_group_sizes(orc, T, G):
+    cfg = variant(2, name=f"g{G}", n_q_heads=2 * G, n_kv_heads=2, n_seq=2, n_keys=700, budget=500,
+                  t_fixed=9000, calib="uniform_r", r_range=(0.6, 0.99), seed=100 + G)
+    run_case(orc, T, cfg)
+
+
+@pytest.mark.parametrize("G,dtype,N", [(8, "bf16", 5000), (4, "bf16", 5000), (3, "f32", 7000), (1, "bf16", 21000)])
+def test_tiled_path_ragged_tail(orc, T, G, dtype, N):
+    cfg = variant(2, name=f"tiled-g{G}-{dtype}-N{N}", n_q_heads=G, n_kv_heads=1, n_seq=3, n_keys=N,
+                  budget=N // 3 + 7, dtype=dtype, t_fixed=N + 1000, calib="head_r", r_range=(0.6, 0.99),
+                  seed=200 + G)
+    run_case(orc, T, cfg)
+
+
+def test_contiguous_positions_config5_shape_small(orc, T):
+    cfg = variant(5, name="c5-shape-small", n_layers=2, n_seq=1, n_keys=4096, budget=384, t_fixed=4095)
+    run_case(orc, T, cfg)
+
+
+def test_budget_one_and_budget_at_least_n(orc, T):
+    run_case(orc, T, variant(2, name="b1", n_q_heads=8, n_kv_heads=2, n_keys=300, budget=1, seed=31))
+    out, _ = run_case(orc, T, variant(2, name="bN", n_q_heads=8, n_kv_heads=2, n_keys=300, budget=300, seed=32))
+    assert np.array_equal(out["kept"], np.tile(np.arange(300), (2, 1)))
+    out, _ = run_case(orc, T, variant(2, name="bbig", n_q_heads=8, n_kv_heads=2, n_keys=300, budget=5000, seed=33))
+    assert np.array_equal(out["kept"], np.tile(np.arange(300), (2, 1)))
+
+
+def test_single_key_stream(orc, T):
+    out, _ = run_case(orc, T, variant(2, name="n1", n_q_heads=4, n_kv_heads=1, n_keys=129, budget=1, seed=34))
+    import torch
+    # one key: its std is zero, z = 0
+    cfg = variant(2, name="n1-exact", n_q_heads=4, n_kv_heads=1, n_keys=1, budget=1, t_fixed=5000, seed=35,
+                  positions="contiguous")
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1)
+    F = T.score(calib, dev["k"], dev["t_dev"], check=True)
+    kept = T.select_topB(F, 1)
+    torch.cuda.synchronize()
+    assert F.cpu().numpy().ravel().tolist() == [0.0]
+    assert kept.cpu().numpy().ravel().tolist() == [0]
+
+
+def _constant_stream_workload(N=500, B=300):
+    cfg = variant(2, name="const", n_q_heads=4, n_kv_heads=2, n_keys=N, budget=B, seed=36)
+    wl = synth.make_host(cfg)
+    k = wl["k"].copy()
+    k[0, 0, 0, :, :] = k[0, 0, 0, 0, :]      # every key of stream 0 identical
+    wl["k"] = k
+    return cfg, wl
+
+
+def test_constant_stream_scores_zero_and_keeps_prefix(orc, T):
+    import torch
+    cfg, wl = _constant_stream_workload()
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads)
+    F = T.score(calib, dev["k"], dev["t_dev"], check=True)
+    kept = T.select_topB(F, cfg.budget)
+    torch.cuda.synchronize()
+    F0 = F.cpu().numpy().reshape(2, -1)[0]
+    assert np.all(F0 == 0.0)
+    assert np.array_equal(kept.cpu().numpy()[0], np.arange(cfg.budget))
+    res = orc.prune_streams(gc.streams_of(wl["k"], cfg.n_keys)[:1], gc.streams_of(wl["pos"], cfg.n_keys)[:1],
+                            wl["t"], wl["qc"], wl["qn"], wl["rb"], cfg.budget, cfg.n_kv_heads, stream_ids=[0])
+    assert np.all(res["F"] == 0.0) and np.array_equal(res["kept"][0], np.arange(cfg.budget))
+
+
+def test_ties_resolved_to_lower_index(orc, T):
+    """Duplicated keys give exactly equal final scores; the selection must take the lower index
+    among equal scores (checked bit-exactly against a full sort of the GPU's own scores)."""
+    import torch
+    cfg = variant(2, name="ties", n_q_heads=8, n_kv_heads=2, n_keys=640, budget=200, seed=37)
+    wl = synth.make_host(cfg)
+    k = wl["k"].copy()
+    k[0, 0, :, 320:, :] = k[0, 0, :, :320, :]          # second half repeats the first half
+    wl["k"] = k
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads)
+    F = T.score(calib, dev["k"], dev["t_dev"], check=True)
+    kept = T.select_topB(F, cfg.budget)
+    torch.cuda.synchronize()
+    Fh = F.cpu().numpy().reshape(2, -1)
+    gc.check_select_exact(orc, kept.cpu().numpy(), Fh, cfg.budget)
+    assert np.array_equal(Fh[:, 320:], Fh[:, :320])
+
+
+def test_nonfinite_key_is_reported(T):
+    import torch
+    cfg = variant(2, name="nan", n_q_heads=4, n_kv_heads=1, n_keys=256, budget=100, seed=38)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    dev["k"][0, 0, 0, 17, 5] = float("nan")
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1)
+    with pytest.raises(T.TriaError) as e:
+        T.score(calib, dev["k"], dev["t_dev"], check=True)
+    assert e.value.status == T.E_NONFINITE
+    # a clean call on the same workspace clears the flag
+    dev2 = synth.to_device(wl)
+    T.score(calib, dev2["k"], dev2["t_dev"], check=True)
+    torch.cuda.synchronize()
+
+
+def test_scores_are_deterministic(T):
+    import torch
+    for cfg in (variant(2, name="det", n_seq=1), variant(2, name="det-tiled", n_q_heads=8, n_kv_heads=1,
+                                                         n_keys=9000, budget=900, t_fixed=12000)):
+        wl = synth.make_host(cfg)
+        dev = synth.to_device(wl)
+        calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads)
+        F1 = T.score(calib, dev["k"], dev["t_dev"], check=True).cpu().numpy()
+        F2 = T.score(calib, dev["k"], dev["t_dev"], check=True).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(F1.view(np.uint32), F2.view(np.uint32))
+
+
+def test_prune_entry_point_matches_separate_calls(T):
+    import torch
+    cfg = variant(2, name="prune", n_seq=2, seed=39)
+    wl = synth.make_host(cfg)
+    d1, d2 = synth.to_device(wl), synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads)
+    F1 = T.score(calib, d1["k"], d1["t_dev"], check=True)
+    kept1 = T.select_topB(F1, cfg.budget)
+    T.compact(d1["k"], d1["v"], d1["pos"], kept1, cfg.budget)
+    F2, kept2 = T.prune(calib, d2["k"], d2["v"], d2["pos"], d2["t_dev"], cfg.budget)
+    torch.cuda.synchronize()
+    assert torch.equal(F1, F2) and torch.equal(kept1, kept2)
+    assert torch.equal(d1["k"], d2["k"]) and torch.equal(d1["v"], d2["v"]) and torch.equal(d1["pos"], d2["pos"])
+
+
+def test_config3_full_size_sampled_streams(orc, T):
+    rng = np.random.default_rng(3)
+    sample = np.sort(rng.choice(synth.CONFIGS[3].n_streams, 24, replace=False))
+    run_case(orc, T, synth.CONFIGS[3], sample=sample)

@@ -226,6 +226,18 @@ def test_zscore_constant_head(orc):
     np.testing.assert_array_equal(F, np.maximum(z[1], 0.0))
 
 
+def test_zscore_rounding_level_spread_is_constant(orc):
+    """Scores equal up to rounding (spread <= 2^-16 of their magnitude) count as constant."""
+    base = 7.25
+    raw = np.vstack([base * (1 + np.linspace(-1, 1, 9) * 2.0 ** -18), np.linspace(-1, 1, 9)])
+    z, F, mu, sd = orc.zmax(raw)
+    assert sd[0] == 0.0 and np.all(z[0] == 0.0)
+    raw2 = np.vstack([base * (1 + np.linspace(-1, 1, 9) * 2.0 ** -12), np.linspace(-1, 1, 9)])
+    z2, _, _, sd2 = orc.zmax(raw2)
+    assert sd2[0] > 0.0
+    np.testing.assert_allclose(z2[0], z2[1], atol=1e-9)
+
+
 def test_zscore_nonfinite_raises(orc):
     raw = np.ones((1, 4))
     raw[0, 2] = np.nan
