@@ -1,0 +1,215 @@
+"""Benchmark of the TriAttention prune step on one MI355X.
+
+One step = tria_score + tria_select_topB + tria_compact over every stream of the workload
+(score every cached key, z-score per query head, GQA max, top-B, in-place compaction of K, V and
+positions).  Default workload: Qwen3-32B shapes, 64 layers x 8 sequences x 8 KV heads
+(4096 streams), 32768 bf16 keys per stream compressed to B = 3072.
+
+Before every step, outside the timed region, K, V and positions are restored from a pristine
+device copy and 1 GiB of scratch is written to evict the 256 MB Infinity Cache and the L2, so
+each step reads a cold, unpruned cache.  Each step is timed with HIP events on the stream the
+kernels run on; the per-phase events (score / select / compact) give the dominant kernel's
+duration for the roofline.
+
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, help="workload id (1..5), see synth.py")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: the prune step runs on one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              "supported (streams shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_compression_tria_amd as T
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    T.lib()   # fail loudly if the HIP library is missing
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    if args.config >= 4:
+        wl = synth.make_device(cfg, dev)
+    else:
+        wl = synth.to_device(synth.make_host(cfg), dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    k, v, pos, t = wl["k"], wl["v"], wl["pos"], wl["t_dev"]
+    k0, v0, pos0 = k.clone(), v.clone(), pos.clone()
+    S, L, Hkv, N, d = k.shape
+    B = cfg.budget
+    n_streams = S * L * Hkv
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], Hkv, cfg.theta)
+    ws = T.workspace(T.score_workspace_bytes(calib, S, N), dev)
+    F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device=dev)
+    kept = torch.empty((n_streams, min(B, N)), dtype=torch.int32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def restore():
+        k.copy_(k0)
+        v.copy_(v0)
+        pos.copy_(pos0)
+        if not args.no_flush:
+            flush.zero_()
+
+    def step():
+        ev[0].record(stream)
+        T.score(calib, k, t, F=F, ws=ws, stream=stream)
+        ev[1].record(stream)
+        T.select_topB(F, B, kept=kept, stream=stream)
+        ev[2].record(stream)
+        T.compact(k, v, pos, kept, B, stream=stream)
+        ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        restore()
+        step()
+    torch.cuda.synchronize()
+    T.score_check(ws)
+
+    phase = np.zeros((args.steps, 3))
+    wall0 = time.time()
+    for i in range(args.steps):
+        restore()
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        phase[i] = [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])]
+    wall_s = time.time() - wall0
+    T.score_check(ws)
+
+    step_ms = phase.sum(axis=1)
+    ms = float(step_ms.mean())
+    total_keys = n_streams * N
+    ar = torch.arange(kept.shape[1], device=dev, dtype=torch.int32)
+    moved = int((kept != ar).sum().item())
+    alg = synth.algorithmic_bytes(cfg, moved)
+    r = d * cfg.elem_bytes
+    score_bytes = n_streams * N * (r + 4)               # K read once, F written once
+    select_bytes = n_streams * N * 4                    # F read once
+    compact_bytes = moved * (4 * r + 8)                 # moved K, V rows and positions, read + written
+    ph = phase.mean(axis=0)
+    phases = {
+        name: {"ms": round(float(t_ms), 4), "alg_bytes": int(b), "GB_s": round(b / (t_ms * 1e-3) / 1e9, 1)}
+        for name, t_ms, b in (("score", ph[0], score_bytes), ("select", ph[1], select_bytes),
+                              ("compact", ph[2], compact_bytes))
+    }
+    dom = max(phases, key=lambda n: phases[n]["ms"])
+    achieved = phases[dom]["GB_s"]
+    out = {
+        "metric": "prune step keys/s (scored + selected + compacted)",
+        "value": round(total_keys / (ms * 1e-3), 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "ms_min": round(float(step_ms.min()), 4),
+        "ms_max": round(float(step_ms.max()), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "streams": n_streams, "keys_per_stream": N, "budget": B,
+                   "layers": L, "seqs": S, "q_heads": cfg.n_q_heads, "kv_heads": Hkv, "head_dim": d,
+                   "cache_dtype": cfg.dtype, "parallelism": "single-gpu"},
+        "alg_bytes_per_step": int(alg),
+        "alg_GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "moved_rows": moved,
+        "phases": phases,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "wall_s_timed_loop_incl_restore": round(wall_s, 3),
+        "gen_s": round(gen_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3))
+    calib.free()
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s):
+    """The fp64 oracle (factored form, OpenMP over streams) on a bounded sample of streams of the
+    same workload, timed on the host cores."""
+    import synth
+    from oracle import oracle
+
+    oracle.build()
+    N, d = cfg.n_keys, cfg.head_dim
+    kk = k0.reshape(-1, N, d)
+    pp = pos0.reshape(-1, N)
+    threads = oracle.max_threads(0)
+
+    def run(ids):
+        kh = synth.cache_to_host(kk[ids[0]:ids[-1] + 1])
+        ph = pp[ids[0]:ids[-1] + 1].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.prune_streams(kh, ph, wl["t"], wl["qc"], wl["qn"], wl["rb"], cfg.budget, cfg.n_kv_heads,
+                             stream_ids=ids, form="fac", n_threads=threads)
+        return time.perf_counter() - t0
+
+    n = max(1, min(threads, kk.shape[0]))
+    dt = run(np.arange(n))
+    if dt < args.cpu_seconds / 2:
+        n2 = int(min(kk.shape[0], max(n, n * args.cpu_seconds / max(dt, 1e-3))))
+        n2 = max(n, (n2 // threads) * threads)
+        if n2 > n:
+            n = n2
+            dt = run(np.arange(n))
+    keys = n * N
+    return {"value": round(keys / dt, 1), "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {kk.shape[0]} streams ({keys} keys), fp64 factored form, {dt:.1f} s",
+            "cpu": cpu_model(), "gpu_over_cpu": round(gpu_keys_s / (keys / dt), 1)}
+
+
+if __name__ == "__main__":
+    main()
