@@ -402,6 +402,22 @@ __global__ __launch_bounds__(kScoreThreads) void zmax_tile_kernel(const float *_
     }
 }
 
+hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
+                       float *stats, hipStream_t st)
+{
+    const long long blocks = (long long)streams * tiles;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    switch (G) {
+#define TRIA_ZMAX_CASE(GG) \
+    case GG: zmax_tile_kernel<GG><<<(unsigned)blocks, kScoreThreads, 0, st>>>(raw, part, N, tiles, F, stats); break;
+    TRIA_ZMAX_CASE(1) TRIA_ZMAX_CASE(2) TRIA_ZMAX_CASE(3) TRIA_ZMAX_CASE(4)
+    TRIA_ZMAX_CASE(5) TRIA_ZMAX_CASE(6) TRIA_ZMAX_CASE(7) TRIA_ZMAX_CASE(8)
+#undef TRIA_ZMAX_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // ---- launch --------------------------------------------------------------------------------
 template <bool BF16, int G>
 static hipError_t launch_score_t(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot,
@@ -431,8 +447,7 @@ static hipError_t launch_score_t(const tria_calib *c, const void *k, int n_seq, 
         (const uint4 *)k, qrot, c->W, c->L, c->Hkv, N, lay.tiles, raw, part, err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    zmax_tile_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(raw, part, N, lay.tiles, F, stats);
-    return hipGetLastError();
+    return launch_zmax(G, raw, part, streams, N, lay.tiles, F, stats, st);
 }
 
 template <bool BF16>
@@ -460,7 +475,8 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
     (void)pos;
     (void)t;
     if (flags != 0) return hipErrorInvalidValue;   // per-key-phase forms: see the variant kernels
-    return dt == TRIA_BF16 ? launch_score_d<true>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st)
+    // bf16 caches score on the matrix cores; fp32 caches on the vector ALU
+    return dt == TRIA_BF16 ? launch_score_mfma(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st)
                            : launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
 }
 

@@ -51,6 +51,10 @@ hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float
 hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st);
+hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
+                             float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
+                       float *stats, hipStream_t st);
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
