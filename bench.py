@@ -84,7 +84,7 @@ def main():
     B = cfg.budget
     n_streams = S * L * Hkv
     calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], Hkv, cfg.theta)
-    ws = T.workspace(T.score_workspace_bytes(calib, S, N), dev)
+    ws = T.workspace(T.score_workspace_bytes(calib, S, N, k.dtype), dev)
     F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device=dev)
     kept = torch.empty((n_streams, min(B, N)), dtype=torch.int32, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -89,8 +89,9 @@ void tria_free_calib(tria_calib *calib);
 /* Shape queries of a loaded table (return -1 for a NULL handle). */
 int tria_calib_dim(const tria_calib *calib, int which /* 0 L, 1 Hq, 2 Hkv, 3 d, 4 G */);
 
-/* Workspace bytes tria_score needs for n_seq sequences of n_keys keys (0 on bad arguments). */
-size_t tria_score_workspace_bytes(const tria_calib *calib, int n_seq, int n_keys);
+/* Workspace bytes tria_score needs for n_seq sequences of n_keys keys of the given cache dtype
+ * (0 on bad arguments). */
+size_t tria_score_workspace_bytes(const tria_calib *calib, tria_dtype dtype, int n_seq, int n_keys);
 
 /*
  * Score every key of every stream and write the final score F (steps 1-2 above).
@@ -138,7 +139,8 @@ tria_status tria_compact(tria_dtype dtype, void *k, void *v, int32_t *pos, const
 
 /* Whole prune step: tria_score, tria_select_topB and tria_compact in sequence on `stream`,
  * with kept written to the caller's buffer.  ws must hold tria_prune_workspace_bytes(). */
-size_t tria_prune_workspace_bytes(const tria_calib *calib, int n_seq, int n_keys, int budget);
+size_t tria_prune_workspace_bytes(const tria_calib *calib, tria_dtype dtype, int n_seq, int n_keys,
+                                  int budget);
 tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void *v, int32_t *pos,
                        const int32_t *t, int n_seq, int n_keys, int budget, float *F,
                        int32_t *kept, unsigned flags, void *ws, size_t ws_bytes, void *stream);

@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.tria_calib_dim.restype = I
         L.tria_calib_dim.argtypes = [P, I]
         L.tria_score_workspace_bytes.restype = S
-        L.tria_score_workspace_bytes.argtypes = [P, I, I]
+        L.tria_score_workspace_bytes.argtypes = [P, I, I, I]
         L.tria_score.restype = I
         L.tria_score.argtypes = [P, I, P, P, P, I, I, P, P, P, U, P, S, P]
         L.tria_score_check.restype = I
@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.tria_compact.restype = I
         L.tria_compact.argtypes = [I, P, P, P, P, I, I, I, I, P]
         L.tria_prune_workspace_bytes.restype = S
-        L.tria_prune_workspace_bytes.argtypes = [P, I, I, I]
+        L.tria_prune_workspace_bytes.argtypes = [P, I, I, I, I]
         L.tria_prune.restype = I
         L.tria_prune.argtypes = [P, I, P, P, P, P, I, I, I, P, P, U, P, S, P]
         L.tria_status_string.restype = ctypes.c_char_p
@@ -161,8 +161,19 @@ def load_calib(q_centre, q_band_norm, r_band, n_kv_heads: int, rope_theta: float
     return Calib(h, L, Hq, int(n_kv_heads))
 
 
-def score_workspace_bytes(calib: Calib, n_seq: int, n_keys: int) -> int:
-    return int(lib().tria_score_workspace_bytes(calib.handle, int(n_seq), int(n_keys)))
+def _dtype_arg(dtype) -> int:
+    import torch
+    if dtype in (BF16, F32):
+        return int(dtype)
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported cache dtype {dtype}")
+
+
+def score_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, dtype=BF16) -> int:
+    return int(lib().tria_score_workspace_bytes(calib.handle, _dtype_arg(dtype), int(n_seq), int(n_keys)))
 
 
 def workspace(nbytes: int, device="cuda"):
@@ -184,7 +195,7 @@ def score(calib: Calib, k, t, F=None, raw=None, head_stats=None, pos=None, flags
     if F is None:
         F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device=k.device)
     if ws is None:
-        ws = workspace(score_workspace_bytes(calib, S, N), k.device)
+        ws = workspace(score_workspace_bytes(calib, S, N, k.dtype), k.device)
     st = lib().tria_score(calib.handle, _dtype_code(k), _ptr(k), _ptr(pos), _ptr(t), S, N, _ptr(F), _ptr(raw),
                           _ptr(head_stats), int(flags), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream))
@@ -225,8 +236,9 @@ def compact(k, v, pos, kept, budget: int, stream=None):
                               d, _stream(stream)), "tria_compact")
 
 
-def prune_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, budget: int) -> int:
-    return int(lib().tria_prune_workspace_bytes(calib.handle, int(n_seq), int(n_keys), int(budget)))
+def prune_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, budget: int, dtype=BF16) -> int:
+    return int(lib().tria_prune_workspace_bytes(calib.handle, _dtype_arg(dtype), int(n_seq), int(n_keys),
+                                                int(budget)))
 
 
 def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int = 0, ws=None, stream=None):
@@ -240,7 +252,7 @@ def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int
     if kept is None:
         kept = torch.empty((S * L * Hkv, min(int(budget), N)), dtype=torch.int32, device=k.device)
     if ws is None:
-        ws = workspace(prune_workspace_bytes(calib, S, N, budget), k.device)
+        ws = workspace(prune_workspace_bytes(calib, S, N, budget, k.dtype), k.device)
     st = lib().tria_prune(calib.handle, _dtype_code(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(t), S, N, int(budget),
                           _ptr(F), _ptr(kept), int(flags), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream))

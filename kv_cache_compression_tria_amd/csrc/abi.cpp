@@ -153,10 +153,10 @@ int tria_calib_dim(const tria_calib *c, int which)
     return -1;
 }
 
-size_t tria_score_workspace_bytes(const tria_calib *c, int n_seq, int n_keys)
+size_t tria_score_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys)
 {
-    if (!c || n_seq <= 0 || n_keys <= 0) return 0;
-    return tria::score_ws_layout(c, n_seq, n_keys).total;
+    if (!c || n_seq <= 0 || n_keys <= 0 || (dt != TRIA_BF16 && dt != TRIA_F32)) return 0;
+    return tria::score_ws_layout(c, dt, n_seq, n_keys).total;
 }
 
 tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
@@ -172,15 +172,16 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     if ((size_t)n_seq * c->L * c->Hkv > (size_t)0x7fffffff) return TRIA_E_INVALID;
     if (!aligned(k, 16) || !aligned(F, 4) || (raw && !aligned(raw, 4)) || (stats && !aligned(stats, 4)))
         return TRIA_E_INVALID;
-    tria_score_ws lay = tria::score_ws_layout(c, n_seq, N);
+    tria_score_ws lay = tria::score_ws_layout(c, dt, n_seq, N);
     if (!ws || ws_bytes < lay.total || !aligned(ws, 256)) return TRIA_E_WORKSPACE;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return TRIA_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
     char *w = (char *)ws;
     float *qrot = (float *)(w + lay.qrot_off);
-    // the rotation kernel also clears the non-finite flag (no memset node, graph-capture safe)
-    if (tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), st) != hipSuccess) return TRIA_E_DEVICE;
+    // the rotation kernel also clears the non-finite flag (no memset node: safe under graph capture)
+    if (tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), st) != hipSuccess)
+        return TRIA_E_DEVICE;
     if (tria::launch_score(c, dt, k, pos, t, n_seq, N, qrot, F, raw, stats, flags, lay, w, st) != hipSuccess)
         return TRIA_E_DEVICE;
     return TRIA_OK;
@@ -228,10 +229,10 @@ tria_status tria_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const in
     return TRIA_OK;
 }
 
-size_t tria_prune_workspace_bytes(const tria_calib *c, int n_seq, int n_keys, int budget)
+size_t tria_prune_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys, int budget)
 {
     if (!c || n_seq <= 0 || n_keys <= 0 || budget <= 0) return 0;
-    return tria_score_workspace_bytes(c, n_seq, n_keys);
+    return tria_score_workspace_bytes(c, dt, n_seq, n_keys);
 }
 
 tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int32_t *pos,

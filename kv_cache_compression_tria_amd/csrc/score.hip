@@ -23,7 +23,7 @@
 
 namespace tria {
 
-tria_score_ws score_ws_layout(const tria_calib *c, int n_seq, int N)
+tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int N)
 {
     tria_score_ws w{};
     const size_t streams = (size_t)n_seq * c->L * c->Hkv;
@@ -36,6 +36,13 @@ tria_score_ws score_ws_layout(const tria_calib *c, int n_seq, int N)
     off = 256;
     w.qrot_off = off;
     off += align256(heads * TRIA_D * sizeof(float));
+    if (dt == TRIA_BF16) {
+        // matrix-core operands of every stream in lane layout, and the per-head pivots
+        w.ops_off = off;
+        off += align256(streams * (size_t)mfma_ops_per_stream(c->G) * 64 * 16);
+        w.pivot_off = off;
+        off += align256(heads * sizeof(float));
+    }
     if (w.tiled) {
         w.raw_off = off;
         off += align256(heads * (size_t)N * sizeof(float));
@@ -55,6 +62,7 @@ __global__ __launch_bounds__(256) void rotate_queries_kernel(const double2 *__re
                                                              int total, float *__restrict__ qrot,
                                                              int *__restrict__ err)
 {
+    // clear the non-finite flag of this call (no memset node)
     if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
     const int gh = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int f = threadIdx.x & 63;
@@ -71,8 +79,7 @@ __global__ __launch_bounds__(256) void rotate_queries_kernel(const double2 *__re
     qrot[(size_t)gh * TRIA_D + TRIA_HALF + f] = (float)(p.x * sn + p.y * cs);
 }
 
-hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err,
-                         hipStream_t st)
+hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, hipStream_t st)
 {
     const int total = n_seq * c->L * c->Hq;
     const int LHq = c->L * c->Hq;

@@ -2,345 +2,510 @@
 //
 // For one stream the G raw scores of key j are (see score.hip for the derivation)
 //     s_h(j) = sum_d Qrot_h[d] * ktilde_j[d]  +  sum_f W_h[f] * |ktilde_{j,f}|
-// i.e. a [keys x 128] x [128 x G] product plus a [keys x 64] x [64 x G] product of the band
-// norms: a dense contraction with a skinny right-hand side.  It runs on
-// v_mfma_f32_16x16x32_bf16 (16 keys x 16 columns x 32-deep per instruction):
-//   * A = the cached bf16 key rows, used as loaded (exact), and the band norms |k_f| computed
-//     in fp32 on the vector ALU and split into SPLIT bf16 terms (hi + lo [+ lo2]);
-//   * B = the per-stream constants Qrot_h and W_h, each split into SPLIT bf16 terms; column
-//     c = b*G + h carries term b of head h, so summing the SPLIT columns of a head recovers the
-//     fp32 constant to 2^-17 (SPLIT = 2) or 2^-26 (SPLIT = 3) relative, accumulation in fp32.
-//     For the norm part only the products of terms a (norm) and b (weight) with a + b < SPLIT
-//     are formed (the rest are below the split's resolution).
+// i.e. a [G x 128] x [128 x keys] product plus a [G x 64] x [64 x keys] product with the band
+// norms: a dense contraction with a skinny left-hand side.  It runs on v_mfma_f32_16x16x32_bf16
+// (16 channels x 16 keys x 32-deep per instruction):
+//   * A = the per-stream constants Qrot_h and W_h, each split into two bf16 terms
+//     c = c0 + c1 (c0 = bf16(c), c1 = bf16(c - c0); |c - c0 - c1| <= 2^-18 |c|).  Term b of head h
+//     is channel 8b + h (heads h >= G are zero rows);
+//   * B = the cached bf16 key rows, used as loaded (exact), and the band norms |k_f| computed in
+//     fp32 on the vector ALU and split the same way; of the four products of the two norm terms
+//     with the two weight terms, the one of the two second terms (below 2^-16 relative) is
+//     dropped.  Accumulation is fp32.
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, element e < 8, r < 4):
 //   A: row l%16, k = 8*(l/16) + e;  B: k = 8*(l/16) + e, column l%16;  D: row 4*(l/16) + r, column l%16.
-// Lane l of a wave loads 16 bytes at byte offset 64*kb + 16*(l/16) (kb < 4) of key row l%16 of
-// the tile: instruction kb reads 64 contiguous bytes of each of 16 rows, and the four loads give
-// MFMA kb its A operand (dims 32kb + 8(l/16) + e).  The lane then also holds, for its 16 bands
-// 8(l/16)+e and 32+8(l/16)+e, both halves (re = dim f, im = dim f+64) of every band: the band
-// norms need no cross-lane exchange.
+// Lane l of a wave loads 16 bytes at byte offset 64*kb + 16*(l/16) (kb < 4) of key row l%16 of a
+// 16-key tile: the four loads give MFMA kb its B operand (dims 32kb + 8(l/16) + e), and the lane
+// then holds, for its 16 bands 8(l/16)+e and 32+8(l/16)+e, both halves (re = dim f, im = dim
+// f+64) of every band: the band norms need no cross-lane exchange.
+// The two terms of a head sit in lanes l and l + 32 (channels 8b + h); one v_permlane32_swap per
+// pair of accumulator registers brings them together, after which lane (g, j) = (l/16, l%16)
+// owns the finished scores of key j for heads hA(g) = 4(g&1) + (g>>1) and hA(g) + 2.
+//
+// The per-stream A operands are built once per call by prep_operands_kernel in exactly this lane
+// layout (one coalesced 16-byte load per lane per MFMA in the scoring kernels), together with a
+// per-head pivot P_h (the fp32 score of the stream's first key; any value near the mean would do).
+// Per-head moments are plain fp64 sums of (s - P_h) and (s - P_h)^2, merged by additions in a
+// fixed order at every level (lane -> wave -> block -> stream): deterministic, no divisions, and
+// no cancellation since P_h lies within the spread of the scores.
 #include "common.cuh"
 #include "tria_internal.h"
 
 namespace tria {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// term b (0-based) of the bf16 expansion x = t0 + t1 + t2 + ... (each residual is exact in fp32)
+constexpr int kOps = 8;     // A operands per stream: 4 trig K-blocks, 2 norm terms x 2 band halves
+
+int mfma_ops_per_stream(int) { return kOps; }
+
+// the first of the two heads owned by lanes of row group g after the combine
+__device__ __forceinline__ int head_a(int g) { return 4 * (g & 1) + (g >> 1); }
+
+// term b (0 or 1) of the bf16 expansion of x
 __device__ __forceinline__ float bf16_term(float x, int b)
 {
-    float r = x;
-    for (int i = 0; i < b; ++i) r = r - (float)(__bf16)r;
-    return (float)(__bf16)r;
+    const float t0 = (float)(__bf16)x;
+    return b == 0 ? t0 : (float)(__bf16)(x - t0);
 }
 
-template <int G, int SPLIT>
-struct MfmaConsts {
-    bf16x8 bt[4];              // trig part, K-block kb: dims 32kb + 8g + e
-    bf16x8 bn[SPLIT][2];       // norm part, norm term a, band half: bands 32*half + 8g + e
-};
-
-// Build this lane's B operands for one stream (qrow: Qrot of head 0 of the group, wrow: W of
-// head 0; consecutive heads are 128 / 64 floats apart).
-template <int G, int SPLIT>
-__device__ __forceinline__ void load_consts(MfmaConsts<G, SPLIT> &c, const float *__restrict__ qrow,
-                                            const float *__restrict__ wrow)
+// ---- prologue: per-stream A operands (lane layout) and pivots ----------------------------------
+// grid = streams, block = 64 (one wave).  ops[(sid*kOps + i)*64 + lane]: operand of MFMA i
+// (i < 4: trig K-block i; 4 + 2a + half: norm term a, band half).
+template <int G>
+__global__ __launch_bounds__(64) void prep_operands_kernel(const u32x4 *__restrict__ k, const float *__restrict__ qrot,
+                                                           const float *__restrict__ W, int L, int Hkv, int N,
+                                                           u32x4 *__restrict__ ops, float *__restrict__ pivot)
 {
-    const int lane = threadIdx.x & 63;
-    const int j = lane & 15, g = lane >> 4;
-    const bool live = j < SPLIT * G;
-    const int b = live ? j / G : 0, h = live ? j % G : 0;
+    const int sid = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int g = sid % Hkv;
+    const int l = (sid / Hkv) % L;
+    const float *qrow = qrot + (size_t)sid * G * TRIA_D;
+    const float *wrow = W + ((size_t)l * Hkv + g) * G * TRIA_HALF;
+    const int j = lane & 15, grp = lane >> 4;
+    const int b = j >> 3, h = j & 7;
+    const bool live = h < G;
+    u32x4 *o = ops + (size_t)sid * kOps * 64 + lane;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+        bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = live ? qrow[h * TRIA_D + 32 * kb + 8 * g + e] : 0.f;
-            c.bt[kb][e] = (__bf16)bf16_term(x, b);
+        for (int e = 0; e < 8; ++e)
+            v[e] = (__bf16)bf16_term(live ? qrow[h * TRIA_D + 32 * kb + 8 * grp + e] : 0.f, b);
+        o[kb * 64] = __builtin_bit_cast(u32x4, v);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (__bf16)bf16_term((live && a + b < 2) ? wrow[h * TRIA_HALF + 32 * half + 8 * grp + e] : 0.f, b);
+            o[(4 + 2 * a + half) * 64] = __builtin_bit_cast(u32x4, v);
         }
-#pragma unroll
-    for (int a = 0; a < SPLIT; ++a)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = (live && a + b < SPLIT) ? wrow[h * TRIA_HALF + 32 * half + 8 * g + e] : 0.f;
-                c.bn[a][half][e] = (__bf16)bf16_term(x, b);
-            }
-}
-
-// Load this lane's 64 bytes of a 16-key tile (zeros for keys at or past `valid`).
-__device__ __forceinline__ void load_tile(u32x4 (&ka)[4], const u32x4 *__restrict__ tile_base, int valid)
-{
-    const int lane = threadIdx.x & 63;
-    const int row = lane & 15, g = lane >> 4;
-    if (row < valid) {
-        const u32x4 *p = tile_base + row * 16 + g;   // row = 16 x 16 B; byte 64kb + 16g = word 4kb + g
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ka[kb] = __builtin_nontemporal_load(p + 4 * kb);
-    } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ka[kb] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < G) {
+        // pivot: the fp32 score of the stream's first key for head `lane`
+        const uint32_t *row = (const uint32_t *)(k + (size_t)sid * N * 16);
+        const float *q = qrow + lane * TRIA_D;
+        const float *w = wrow + lane * TRIA_HALF;
+        float s = 0.f;
+        for (int f = 0; f < TRIA_HALF; f += 2) {
+            const uint32_t x = row[f / 2], y = row[(TRIA_HALF + f) / 2];
+            const float re0 = bf16_lo(x), re1 = bf16_hi(x), im0 = bf16_lo(y), im1 = bf16_hi(y);
+            s = fmaf(q[f], re0, s);
+            s = fmaf(q[f + 1], re1, s);
+            s = fmaf(q[TRIA_HALF + f], im0, s);
+            s = fmaf(q[TRIA_HALF + f + 1], im1, s);
+            s = fmaf(w[f], sqrtf(re0 * re0 + im0 * im0), s);
+            s = fmaf(w[f + 1], sqrtf(re1 * re1 + im1 * im1), s);
+        }
+        pivot[(size_t)sid * G + lane] = isfinite(s) ? s : 0.f;
     }
 }
 
-// Raw scores of one 16-key tile.  Returns D: lane l holds, for keys 4*(l/16) + r, the sum of
-// columns l%16: after combine_columns the lanes with l%16 < G hold head l%16.
-template <int G, int SPLIT>
-__device__ __forceinline__ floatx4 score_tile16(const u32x4 (&ka)[4], const MfmaConsts<G, SPLIT> &c)
+struct Ops {
+    bf16x8 at[4];       // trig part, K-block kb: dims 32kb + 8g + e
+    bf16x8 an[2][2];    // norm part, norm term a, band half: bands 32*half + 8g + e
+};
+
+__device__ __forceinline__ void load_ops(Ops &c, const u32x4 *__restrict__ ops_stream)
+{
+    const int lane = threadIdx.x & 63;
+    const u32x4 *o = ops_stream + lane;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) c.at[kb] = __builtin_bit_cast(bf16x8, o[kb * 64]);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) c.an[a][half] = __builtin_bit_cast(bf16x8, o[(4 + 2 * a + half) * 64]);
+}
+
+// Load this lane's 64 bytes of a 16-key tile.  Rows at or past `valid` re-read row 0 of the tile
+// (always a real row): their output columns are discarded, and keeping the load unconditional
+// keeps the wait counts of the software pipeline exact.
+__device__ __forceinline__ void load_tile(u32x4 (&ka)[4], const u32x4 *__restrict__ tile_base, int valid)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = (lane & 15) < valid ? (lane & 15) : 0, g = lane >> 4;
+    const u32x4 *p = tile_base + row * 16 + g;   // row = 16 x 16 B; byte 64kb + 16g = word 4kb + g
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) ka[kb] = __builtin_nontemporal_load(p + 4 * kb);
+}
+
+// v_permlane32_swap: lanes 32..63 of x trade places with lanes 0..31 of y, so that afterwards
+// x = (x[0..31], y[0..31]) and y = (x[32..63], y[32..63]).  Written as inline asm because the
+// compiler's builtin for it drops its second result; the s_nop pairs cover the wait states
+// around a cross-lane VALU operation.
+__device__ __forceinline__ void permlane32_swap(float &x, float &y)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+
+// re^2 + im^2 of a band held as a bf16 pair (re, im) in fp32 (v_dot2: products exact, one
+// rounding)
+__device__ __forceinline__ float band_sq(uint32_t pair)
+{
+    const bf16x2 p = __builtin_bit_cast(bf16x2, pair);
+    return __builtin_amdgcn_fdot2_f32_bf16(p, p, 0.f, false);
+}
+
+// Scores of one 16-key tile: lane (g, j) returns v[0], v[1] = heads head_a(g), head_a(g) + 2 of
+// key j (zero for heads >= G).
+__device__ __forceinline__ void score_tile16(const u32x4 (&ka)[4], const Ops &c, float (&v)[2])
 {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kb]), c.bt[kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[kb], __builtin_bit_cast(bf16x8, ka[kb]), acc, 0, 0, 0);
 
-    // band norms of bands 8g+e (re: ka[0], im: ka[2]) and 32+8g+e (re: ka[1], im: ka[3])
-    float n[2][8];
+    // band norms: bands 8g+e (re in ka[0], im in ka[2]) and 32+8g+e (re in ka[1], im in ka[3]);
+    // v_perm pairs (re, im) of a band, v_dot2 forms re^2 + im^2 from the bf16 halves in fp32,
+    // and the two-term split of a pair of norms costs two packed conversions, a shift, a mask
+    // and two subtractions
+    u32x4 t0[2], t1[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const u32x4 x = ka[half], y = ka[2 + half];
-        const uint32_t xs[4] = {x[0], x[1], x[2], x[3]}, ys[4] = {y[0], y[1], y[2], y[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float r0 = bf16_lo(xs[i]), r1 = bf16_hi(xs[i]);
-            const float i0 = bf16_lo(ys[i]), i1 = bf16_hi(ys[i]);
-            n[half][2 * i] = __builtin_amdgcn_sqrtf(fmaf(r0, r0, i0 * i0));
-            n[half][2 * i + 1] = __builtin_amdgcn_sqrtf(fmaf(r1, r1, i1 * i1));
+            const uint32_t p0 = __builtin_amdgcn_perm(y[i], x[i], 0x05040100u);
+            const uint32_t p1 = __builtin_amdgcn_perm(y[i], x[i], 0x07060302u);
+            const float n0 = __builtin_amdgcn_sqrtf(band_sq(p0));
+            const float n1 = __builtin_amdgcn_sqrtf(band_sq(p1));
+            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{n0, n1}, bf16x2));
+            const float r0 = n0 - __builtin_bit_cast(float, hi << 16);
+            const float r1 = n1 - __builtin_bit_cast(float, hi & 0xffff0000u);
+            t0[half][i] = hi;
+            t1[half][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r0, r1}, bf16x2));
         }
     }
 #pragma unroll
-    for (int a = 0; a < SPLIT; ++a)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            bf16x8 t;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 v = (__bf16)n[half][e];
-                t[e] = v;
-                n[half][e] -= (float)v;        // exact residual for the next term
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t, c.bn[a][half], acc, 0, 0, 0);
-        }
-    return acc;
-}
-
-// Sum the SPLIT columns of each head into the lanes with l%16 < G.
-template <int G, int SPLIT>
-__device__ __forceinline__ floatx4 combine_columns(floatx4 acc)
-{
-    const int lane = threadIdx.x & 63;
-    floatx4 s = acc;
-#pragma unroll
-    for (int b = 1; b < SPLIT; ++b) {
-        const int src = (lane & 48) | (((lane & 15) + b * G) & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] += __shfl(acc[r], src, 64);
+    for (int half = 0; half < 2; ++half) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[0][half], __builtin_bit_cast(bf16x8, t0[half]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[1][half], __builtin_bit_cast(bf16x8, t1[half]), acc, 0, 0, 0);
     }
-    return s;
+
+    // lanes l < 32 hold term 0 of channels 4g + r, lanes l + 32 term 1 of the same heads
+    float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+    permlane32_swap(a0, a1);
+    permlane32_swap(a2, a3);
+    v[0] = a0 + a1;
+    v[1] = a2 + a3;
 }
 
-// Running moments of one head over the values a lane sees: sums of (v - p) and (v - p)^2 in fp64
-// around a pivot p (the lane's first value), so the variance does not cancel; min and max.
-struct Moments {
-    double n, s1, s2;
-    float p, mn, mx;
-    __device__ void init() { n = 0.0; s1 = 0.0; s2 = 0.0; p = 0.f; mn = INFINITY; mx = -INFINITY; }
-    __device__ void add(float v)
+// Moments of one head around the stream pivot P: S1 = sum (v - P), S2 = sum (v - P)^2 (fp64),
+// min, max.  Merging two is an addition; the count is known from the key ranges.  A non-finite
+// score makes S1 or S2 non-finite.
+struct Sums {
+    double s1, s2;
+    float mn, mx;
+    __device__ void init() { s1 = 0.0; s2 = 0.0; mn = INFINITY; mx = -INFINITY; }
+    __device__ void add(float v, float p)
     {
-        if (n == 0.0) p = v;
-        const double d = (double)v - (double)p;
-        n += 1.0;
+        const double d = (double)(v - p);
         s1 += d;
         s2 = fma(d, d, s2);
         mn = fminf(mn, v);
         mx = fmaxf(mx, v);
     }
-    __device__ double mean() const { return n > 0.0 ? (double)p + s1 / n : 0.0; }
-    __device__ double m2() const { return n > 0.0 ? fmax(s2 - s1 * (s1 / n), 0.0) : 0.0; }
-};
-
-// (count, mean, M2, min, max) with Chan et al.'s pairwise merge.
-struct Merged {
-    double n, mean, m2;
-    float mn, mx;
-    __device__ void init() { n = 0.0; mean = 0.0; m2 = 0.0; mn = INFINITY; mx = -INFINITY; }
-    __device__ void merge(double nb, double meanb, double m2b, float mnb, float mxb)
+    __device__ void add(const Sums &o)
     {
-        if (nb == 0.0) return;
-        const double tot = n + nb;
-        const double delta = meanb - mean;
-        mean += delta * (nb / tot);
-        m2 += m2b + delta * delta * (n * nb / tot);
-        n = tot;
-        mn = fminf(mn, mnb);
-        mx = fmaxf(mx, mxb);
+        s1 += o.s1;
+        s2 += o.s2;
+        mn = fminf(mn, o.mn);
+        mx = fmaxf(mx, o.mx);
     }
 };
 
-// Merge the moments of the 4 lanes of a wave that hold the same head (lanes h, h+16, h+32, h+48).
-__device__ __forceinline__ Merged wave_merge_heads(const Moments &m)
+// Sum over the 16 lanes of a wave row (same l/16), fixed butterfly order: every lane of the row
+// ends with the same bits (IEEE addition is commutative).
+__device__ __forceinline__ void row16_sum(Sums &m)
 {
-    Merged a;
-    a.n = m.n; a.mean = m.mean(); a.m2 = m.m2(); a.mn = m.mn; a.mx = m.mx;
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-        const double nb = __shfl_xor(a.n, o, 64), meanb = __shfl_xor(a.mean, o, 64), m2b = __shfl_xor(a.m2, o, 64);
-        const float mnb = __shfl_xor(a.mn, o, 64), mxb = __shfl_xor(a.mx, o, 64);
-        a.merge(nb, meanb, m2b, mnb, mxb);
+    for (int o = 1; o < 16; o <<= 1) {
+        Sums t;
+        t.s1 = __shfl_xor(m.s1, o, 64);
+        t.s2 = __shfl_xor(m.s2, o, 64);
+        t.mn = __shfl_xor(m.mn, o, 64);
+        t.mx = __shfl_xor(m.mx, o, 64);
+        m.add(t);
     }
-    return a;
 }
 
+// A head whose scores span at most 2^-16 of their largest magnitude is constant (scores equal up
+// to rounding): std := 0, z := 0.
 __device__ __forceinline__ bool flat_head_m(double mn, double mx)
 {
     return (mx - mn) <= ldexp(fmax(fabs(mn), fabs(mx)), -16);
 }
 
-// ---- tiled path: block = (stream, 1024-key tile); raw scores to the workspace ------------------
-template <int G, int SPLIT>
-__global__ __launch_bounds__(kScoreThreads) void score_mfma_tile_kernel(
-    const u32x4 *__restrict__ k, const float *__restrict__ qrot, const float *__restrict__ W, int L, int Hkv,
-    int N, int tiles, float *__restrict__ raw, double *__restrict__ part, int *__restrict__ err)
+// mean and (population) std of n values from their sums around p
+__device__ __forceinline__ void finish_moments(const Sums &m, double p, double n, double &mean, double &sd)
 {
-    __shared__ double sm_n[4][G], sm_mean[4][G], sm_m2[4][G];
-    __shared__ float sm_mn[4][G], sm_mx[4][G];
+    mean = p + m.s1 / n;
+    const double m2 = fmax(m.s2 - m.s1 * (m.s1 / n), 0.0);
+    sd = flat_head_m((double)m.mn, (double)m.mx) ? 0.0 : sqrt(m2 / n);
+}
+
+// Per-block reduction of the lane sums: waves publish their 16-lane row sums to LDS, thread h
+// (< G) adds the 4 waves in order.
+struct BlockSums {
+    double s1[4][8], s2[4][8];
+    float mn[4][8], mx[4][8];
+};
+
+__device__ __forceinline__ void block_sums_stage(BlockSums &bs, Sums (&m)[2])
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        row16_sum(m[s]);
+        const int h = head_a(g) + 2 * s;
+        if (j == 0) {
+            bs.s1[wid][h] = m[s].s1;
+            bs.s2[wid][h] = m[s].s2;
+            bs.mn[wid][h] = m[s].mn;
+            bs.mx[wid][h] = m[s].mx;
+        }
+    }
+}
+
+__device__ __forceinline__ Sums block_sums_of(const BlockSums &bs, int h)
+{
+    Sums t;
+    t.init();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        Sums u;
+        u.s1 = bs.s1[w][h]; u.s2 = bs.s2[w][h]; u.mn = bs.mn[w][h]; u.mx = bs.mx[w][h];
+        t.add(u);
+    }
+    return t;
+}
+
+// Everything one wave needs to score 16-key tiles of a stream: operands, pivots of its two heads
+// and running sums.
+template <int G>
+struct WaveScorer {
+    Ops c;
+    float p[2];
+    Sums m[2];
+
+    __device__ void begin(const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int sid)
+    {
+        load_ops(c, ops + (size_t)sid * kOps * 64);
+        const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int h = head_a(g) + 2 * s;
+            p[s] = pivot[(size_t)sid * G + (h < G ? h : 0)];
+            m[s].init();
+        }
+    }
+    // score a tile; v[s] = score of key (tile row l%16) for head head_a(g) + 2s.  Rows >= nvalid
+    // and heads >= G enter the sums as the pivot itself (no change to the sums; the pivot is the
+    // score of key 0, so min and max keep their values): no branches in the key loop.
+    __device__ void score(const u32x4 (&b)[4], int nvalid, float (&v)[2])
+    {
+        score_tile16(b, c, v);
+        const int lane = threadIdx.x & 63;
+        const int j = lane & 15, ha = head_a(lane >> 4);
+        const bool ok = j < nvalid;
+        m[0].add((ok && ha < G) ? v[0] : p[0], p[0]);
+        m[1].add((ok && ha + 2 < G) ? v[1] : p[1], p[1]);
+    }
+};
+
+// Four-deep ring of tile registers, straight-line: item i of a wave lives in buffer i % 4 and is
+// loaded three items ahead of its use.  issue(b, i) loads item i; compute(b, i) scores it.  The
+// item count is rounded up to a multiple of four so that the loop body has no exits: items past
+// the end re-read a real tile and are scored as empty (no valid rows).  With no branch between a
+// load and its use the compiler cannot sink the loads next to their uses; TRIA_PIN (a scheduling
+// barrier, no instruction) keeps the machine scheduler from regrouping them.
+#define TRIA_PIN() __builtin_amdgcn_sched_barrier(0)
+#define TRIA_RING4(nt, issue, compute)                                                         \
+    do {                                                                                       \
+        u32x4 b0_[4], b1_[4], b2_[4], b3_[4];                                                  \
+        const int n4_ = ((nt) + 3) & ~3;                                                       \
+        issue(b0_, 0);                                                                         \
+        TRIA_PIN();                                                                            \
+        issue(b1_, 1);                                                                         \
+        TRIA_PIN();                                                                            \
+        issue(b2_, 2);                                                                         \
+        TRIA_PIN();                                                                            \
+        for (int i_ = 0; i_ < n4_; i_ += 4) {                                                  \
+            issue(b3_, i_ + 3);                                                                \
+            TRIA_PIN();                                                                        \
+            compute(b0_, i_);                                                                  \
+            issue(b0_, i_ + 4);                                                                \
+            TRIA_PIN();                                                                        \
+            compute(b1_, i_ + 1);                                                              \
+            issue(b1_, i_ + 5);                                                                \
+            TRIA_PIN();                                                                        \
+            compute(b2_, i_ + 2);                                                              \
+            issue(b2_, i_ + 6);                                                                \
+            TRIA_PIN();                                                                        \
+            compute(b3_, i_ + 3);                                                              \
+        }                                                                                      \
+    } while (0)
+
+// ---- tiled path: block = (stream, 1024-key tile); raw scores key-major through the workspace ---
+// raw [streams][N][G]; partial sums per (stream, tile, head): s1, s2, min, max.
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_mfma_tile_kernel(
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N, int tiles,
+    float *__restrict__ raw, double *__restrict__ part)
+{
+    __shared__ BlockSums bs;
     const int sid = blockIdx.x / tiles;
     const int tile = blockIdx.x - sid * tiles;
-    const int g = sid % Hkv;
-    const int l = (sid / Hkv) % L;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar loop control
+    const int jj = lane & 15, ha = head_a(lane >> 4);
 
-    MfmaConsts<G, SPLIT> c;
-    load_consts<G, SPLIT>(c, qrot + (size_t)sid * G * TRIA_D, W + ((size_t)l * Hkv + g) * G * TRIA_HALF);
+    WaveScorer<G> ws;
+    ws.begin(ops, pivot, sid);
 
     const int j0 = tile * kTileKeys;
     const int nkeys = min(kTileKeys, N - j0);
     const int ntiles16 = (nkeys + 15) >> 4;
     const u32x4 *kb = k + ((size_t)sid * N + j0) * 16;
-    Moments m;
-    m.init();
-    bool bad = false;
-    const bool vec4 = (N & 3) == 0 && ((uintptr_t)raw & 15) == 0;
-    u32x4 cur[4];
-    int t = wid;
-    if (t < ntiles16) load_tile(cur, kb + (size_t)t * 16 * 16, nkeys - t * 16);
-    for (; t < ntiles16; t += 4) {
-        u32x4 nxt[4];
-        const int tn = t + 4;
-        if (tn < ntiles16) load_tile(nxt, kb + (size_t)tn * 16 * 16, nkeys - tn * 16);
-        floatx4 acc = score_tile16<G, SPLIT>(cur, c);
-        acc = combine_columns<G, SPLIT>(acc);
-        if (col < G) {
-            const int key = t * 16 + 4 * grp;                    // first of this lane's 4 keys
-            float *dst = raw + ((size_t)sid * G + col) * N + j0 + key;
-            const int nv = min(4, nkeys - key);
-            if (nv == 4 && vec4) {
-                *(float4 *)dst = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (r < nv) dst[r] = acc[r];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (r < nv) {
-                    bad |= !isfinite(acc[r]);
-                    m.add(acc[r]);
-                }
-        }
-        if (tn < ntiles16) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
-        }
-    }
-    if (bad) atomicOr(err, 1);
-    const Merged wm = wave_merge_heads(m);
-    if (lane < G) {
-        sm_n[wid][lane] = wm.n; sm_mean[wid][lane] = wm.mean; sm_m2[wid][lane] = wm.m2;
-        sm_mn[wid][lane] = wm.mn; sm_mx[wid][lane] = wm.mx;
-    }
+    const int nt_w = wid < ntiles16 ? (ntiles16 - wid + 3) >> 2 : 0;
+    // raw scores of this block's keys through a buffer resource sized to them: stores of rows
+    // past the end (ragged last tile) and of heads >= G (offset pushed past the end) are dropped
+    // by the hardware, so every tile issues the same two stores and the key loop has no branches
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(raw + ((size_t)sid * N + j0) * G, 0, nkeys * G * 4, 0x00020000);
+    const int off0 = ha < G ? (jj * G + ha) * 4 : 1 << 30;
+    const int off1 = ha + 2 < G ? (jj * G + ha + 2) * 4 : 1 << 30;
+    // item i of this wave is tile wid + 4i
+    auto issue = [&](u32x4 (&b)[4], int i) {
+        const int t = min(wid + 4 * i, ntiles16 - 1);
+        load_tile(b, kb + (size_t)t * 16 * 16, nkeys - t * 16);
+    };
+    auto compute = [&](const u32x4 (&b)[4], int i) {
+        const int t = wid + 4 * i;
+        float v[2];
+        ws.score(b, nkeys - t * 16, v);
+        // the whole offset goes in the vector operand: the range check does not include soffset
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[0]), rsrc, off0 + t * 16 * G * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[1]), rsrc, off1 + t * 16 * G * 4, 0, 0);
+    };
+    if (nt_w > 0) TRIA_RING4(nt_w, issue, compute);
+    block_sums_stage(bs, ws.m);
     __syncthreads();
     if (threadIdx.x < G) {
         const int h = threadIdx.x;
-        Merged t2;
+        const Sums t2 = block_sums_of(bs, h);
+        double *q = part + (((size_t)sid * tiles + tile) * G + h) * 4;
+        q[0] = t2.s1;
+        q[1] = t2.s2;
+        q[2] = (double)t2.mn;
+        q[3] = (double)t2.mx;
+    }
+}
+
+// Normalisation of the tiled path: adds the stream's tile partials in order, then F for this
+// block's 1024 keys from the key-major raw scores (and the optional head-major raw output).
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void zmax_keymajor_kernel(
+    const float *__restrict__ raw, const double *__restrict__ part, const float *__restrict__ pivot, int N,
+    int tiles, float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats,
+    int *__restrict__ err)
+{
+    __shared__ float zmu[G], zinv[G];
+    const int sid = blockIdx.x / tiles;
+    const int tile = blockIdx.x - sid * tiles;
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        Sums t2;
         t2.init();
-        for (int w = 0; w < 4; ++w) t2.merge(sm_n[w][h], sm_mean[w][h], sm_m2[w][h], sm_mn[w][h], sm_mx[w][h]);
-        double *p = part + (((size_t)sid * tiles + tile) * G + h) * 4;
-        p[0] = t2.mean;
-        p[1] = t2.m2;
-        p[2] = (double)t2.mn;
-        p[3] = (double)t2.mx;
+        for (int tt = 0; tt < tiles; ++tt) {
+            const double *q = part + (((size_t)sid * tiles + tt) * G + h) * 4;
+            Sums u;
+            u.s1 = q[0]; u.s2 = q[1]; u.mn = (float)q[2]; u.mx = (float)q[3];
+            t2.add(u);
+        }
+        if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
+        double mean, sd;
+        finish_moments(t2, (double)pivot[(size_t)sid * G + h], (double)N, mean, sd);
+        zmu[h] = (float)mean;
+        zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
+        if (stats && tile == 0) {
+            stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
+            stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
+        }
+    }
+    __syncthreads();
+    const int j0 = tile * kTileKeys;
+    const int nkeys = min(kTileKeys, N - j0);
+    for (int j = threadIdx.x; j < nkeys; j += kScoreThreads) {
+        const float *r = raw + ((size_t)sid * N + j0 + j) * G;
+        float z = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < G; ++h) z = fmaxf(z, (r[h] - zmu[h]) * zinv[h]);
+        F[(size_t)sid * N + j0 + j] = z;
+        if (raw_out)
+#pragma unroll
+            for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + j0 + j] = r[h];
     }
 }
 
 // ---- fused path: one block per stream, raw scores kept in LDS ---------------------------------
-template <int G, int SPLIT>
+template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_mfma_fused_kernel(
-    const u32x4 *__restrict__ k, const float *__restrict__ qrot, const float *__restrict__ W, int L, int Hkv,
-    int N, float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats, int *__restrict__ err)
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
+    float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats, int *__restrict__ err)
 {
     extern __shared__ float raw[];                 // [G][NP], NP = N | 1 (odd stride: no bank conflicts)
     const int NP = N | 1;
-    __shared__ double sm_n[4][G], sm_mean[4][G], sm_m2[4][G];
-    __shared__ float sm_mn[4][G], sm_mx[4][G];
+    __shared__ BlockSums bs;
     __shared__ float zmu[G], zinv[G];
     const int sid = blockIdx.x;
-    const int g = sid % Hkv;
-    const int l = (sid / Hkv) % L;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jj = lane & 15, ha = head_a(lane >> 4);
 
-    MfmaConsts<G, SPLIT> c;
-    load_consts<G, SPLIT>(c, qrot + (size_t)sid * G * TRIA_D, W + ((size_t)l * Hkv + g) * G * TRIA_HALF);
+    WaveScorer<G> ws;
+    ws.begin(ops, pivot, sid);
 
     const int ntiles16 = (N + 15) >> 4;
     const u32x4 *kb = k + (size_t)sid * N * 16;
-    Moments m;
-    m.init();
-    bool bad = false;
-    u32x4 cur[4];
-    int t = wid;
-    if (t < ntiles16) load_tile(cur, kb + (size_t)t * 16 * 16, N - t * 16);
-    for (; t < ntiles16; t += 4) {
-        u32x4 nxt[4];
-        const int tn = t + 4;
-        if (tn < ntiles16) load_tile(nxt, kb + (size_t)tn * 16 * 16, N - tn * 16);
-        floatx4 acc = score_tile16<G, SPLIT>(cur, c);
-        acc = combine_columns<G, SPLIT>(acc);
-        if (col < G) {
-            const int key = t * 16 + 4 * grp;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (key + r < N) {
-                    raw[col * NP + key + r] = acc[r];
-                    bad |= !isfinite(acc[r]);
-                    m.add(acc[r]);
-                }
+    const int nt_w = wid < ntiles16 ? (ntiles16 - wid + 3) >> 2 : 0;
+    auto issue = [&](u32x4 (&b)[4], int i) {
+        const int t = min(wid + 4 * i, ntiles16 - 1);
+        load_tile(b, kb + (size_t)t * 16 * 16, N - t * 16);
+    };
+    auto compute = [&](const u32x4 (&b)[4], int i) {
+        const int t = wid + 4 * i;
+        float v[2];
+        ws.score(b, N - t * 16, v);
+        const int key = t * 16 + jj;
+        if (key < N) {
+            if (ha < G) raw[ha * NP + key] = v[0];
+            if (ha + 2 < G) raw[(ha + 2) * NP + key] = v[1];
         }
-        if (tn < ntiles16) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
-        }
-    }
-    if (bad) atomicOr(err, 1);
-    const Merged wm = wave_merge_heads(m);
-    if (lane < G) {
-        sm_n[wid][lane] = wm.n; sm_mean[wid][lane] = wm.mean; sm_m2[wid][lane] = wm.m2;
-        sm_mn[wid][lane] = wm.mn; sm_mx[wid][lane] = wm.mx;
-    }
+    };
+    if (nt_w > 0) TRIA_RING4(nt_w, issue, compute);
+    block_sums_stage(bs, ws.m);
     __syncthreads();
     if (threadIdx.x < G) {
         const int h = threadIdx.x;
-        Merged t2;
-        t2.init();
-        for (int w = 0; w < 4; ++w) t2.merge(sm_n[w][h], sm_mean[w][h], sm_m2[w][h], sm_mn[w][h], sm_mx[w][h]);
-        const double sd = flat_head_m((double)t2.mn, (double)t2.mx) ? 0.0 : sqrt(t2.m2 / (double)N);
-        zmu[h] = (float)t2.mean;
+        const Sums t2 = block_sums_of(bs, h);
+        if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
+        double mean, sd;
+        finish_moments(t2, (double)pivot[(size_t)sid * G + h], (double)N, mean, sd);
+        zmu[h] = (float)mean;
         zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
         if (stats) {
-            stats[((size_t)sid * G + h) * 2 + 0] = (float)t2.mean;
+            stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
             stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
         }
     }
@@ -362,31 +527,36 @@ template <int G>
 static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
                                 float *raw_out, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
-    constexpr int SPLIT = 3 * G <= 16 ? 3 : 2;
     const int streams = n_seq * c->L * c->Hkv;
     int *err = (int *)(ws + lay.err_off);
+    const u32x4 *kp = (const u32x4 *)k;
+    u32x4 *ops = (u32x4 *)(ws + lay.ops_off);
+    float *pivot = (float *)(ws + lay.pivot_off);
+    prep_operands_kernel<G><<<streams, 64, 0, st>>>(kp, qrot, c->W, c->L, c->Hkv, N, ops, pivot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (!lay.tiled) {
         const size_t lds = (size_t)G * (N | 1) * 4;
         static bool attr_set = false;
         if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)score_mfma_fused_kernel<G, SPLIT>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsMax);
+            e = hipFuncSetAttribute((const void *)score_mfma_fused_kernel<G>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kFusedLdsMax);
             if (e != hipSuccess) return e;
             attr_set = true;
         }
-        score_mfma_fused_kernel<G, SPLIT><<<streams, kScoreThreads, lds, st>>>(
-            (const u32x4 *)k, qrot, c->W, c->L, c->Hkv, N, F, raw_out, stats, err);
+        score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
-    float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
+    float *raw = (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
     const long long blocks = (long long)streams * lay.tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    score_mfma_tile_kernel<G, SPLIT><<<(unsigned)blocks, kScoreThreads, 0, st>>>(
-        (const u32x4 *)k, qrot, c->W, c->L, c->Hkv, N, lay.tiles, raw, part, err);
-    hipError_t e = hipGetLastError();
+    score_mfma_tile_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(kp, ops, pivot, N, lay.tiles, raw, part);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_zmax(c->G, raw, part, streams, N, lay.tiles, F, stats, st);
+    zmax_keymajor_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(raw, part, pivot, N, lay.tiles, F, raw_out,
+                                                                        stats, err);
+    return hipGetLastError();
 }
 
 hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,

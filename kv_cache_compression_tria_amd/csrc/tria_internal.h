@@ -27,9 +27,9 @@ struct tria_calib {
 
 // Workspace layout of tria_score (every region 256-byte aligned).
 struct tria_score_ws {
-    size_t qrot_off, raw_off, part_off, err_off, total;
-    int tiled;       // 1: raw scores round-trip through the workspace (large streams)
-    int tiles;       // key tiles per stream on the tiled path
+    size_t qrot_off, raw_off, part_off, err_off, ops_off, pivot_off, total;
+    int tiled;       // 1: the stream does not fit one block's LDS
+    int tiles;       // key tiles (blocks) per stream on the tiled path
 };
 
 namespace tria {
@@ -44,13 +44,14 @@ constexpr int kCompactRows = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-tria_score_ws score_ws_layout(const tria_calib *c, int n_seq, int n_keys);
+tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys);
 
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, hipStream_t st);
 hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st);
+int mfma_ops_per_stream(int G);   // 16-byte operand words per lane and stream (prologue output)
 hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
                              float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
 hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,

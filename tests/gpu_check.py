@@ -28,7 +28,7 @@ def gpu_prune(T, calib, dev, budget, want_raw=True, flags=0):
     Hq = calib.n_q_heads
     raw = torch.empty((S, L, Hq, N), dtype=torch.float32, device=k.device) if want_raw else None
     stats = torch.empty((S, L, Hq, 2), dtype=torch.float32, device=k.device)
-    ws = T.workspace(T.score_workspace_bytes(calib, S, N), k.device)
+    ws = T.workspace(T.score_workspace_bytes(calib, S, N, k.dtype), k.device)
     F = T.score(calib, k, t, raw=raw, head_stats=stats, pos=pos, flags=flags, ws=ws)
     T.score_check(ws)
     kept = T.select_topB(F, budget)

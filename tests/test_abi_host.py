@@ -92,7 +92,7 @@ def test_score_select_compact_validation(tria):
     L = tria.lib()
     fake = ctypes.c_void_p(0x1000)    # never dereferenced: validation fails first
     assert L.tria_score(None, 0, fake, None, fake, 1, 16, fake, None, None, 0, fake, 1 << 20, None) == tria.E_INVALID
-    assert L.tria_score_workspace_bytes(None, 1, 16) == 0
+    assert L.tria_score_workspace_bytes(None, 0, 1, 16) == 0
     assert L.tria_select_topB(None, 1, 16, 4, fake, fake, 256, None) == tria.E_INVALID
     assert L.tria_select_topB(fake, 1, 0, 4, fake, fake, 256, None) == tria.E_INVALID
     assert L.tria_select_topB(fake, 1, 16, 0, fake, fake, 256, None) == tria.E_INVALID

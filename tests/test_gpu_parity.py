@@ -82,6 +82,21 @@ def test_tiled_path_ragged_tail(orc, T, G, dtype, N):
     run_case(orc, T, cfg)
 
 
+def test_tiled_path_long_stream(orc, T):
+    """A stream of 70001 keys: 69 tiles of 1024 keys, the last one ragged (369 keys)."""
+    cfg = variant(2, name="tiled-long", n_q_heads=2, n_kv_heads=1, n_seq=1, n_keys=70001, budget=7000,
+                  t_fixed=90000, calib="head_r", r_range=(0.6, 0.99), seed=210)
+    run_case(orc, T, cfg)
+
+
+def test_tiled_path_many_streams_ragged_tail(orc, T):
+    """40 streams of 65236 keys (63 * 1024 + 724): every stream ends in a ragged tile."""
+    cfg = variant(2, name="tiled-many", n_q_heads=16, n_kv_heads=8, n_seq=5, n_layers=1, n_keys=65236,
+                  budget=6000, t_fixed=70000, calib="head_r", r_range=(0.6, 0.99), seed=211)
+    rng = np.random.default_rng(211)
+    run_case(orc, T, cfg, sample=np.sort(rng.choice(cfg.n_streams, 5, replace=False)))
+
+
 def test_contiguous_positions_config5_shape_small(orc, T):
     cfg = variant(5, name="c5-shape-small", n_layers=2, n_seq=1, n_keys=4096, budget=384, t_fixed=4095)
     run_case(orc, T, cfg)
