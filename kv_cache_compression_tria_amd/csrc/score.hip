@@ -48,6 +48,8 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
         off += align256(heads * (size_t)N * sizeof(float));
         w.part_off = off;
         off += align256(streams * (size_t)w.tiles * c->G * 4 * sizeof(double));
+        w.zst_off = off;
+        off += align256(heads * 2 * sizeof(float));
     }
     w.total = off;
     return w;

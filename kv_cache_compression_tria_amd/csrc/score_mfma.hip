@@ -28,6 +28,8 @@
 // Per-head moments are plain fp64 sums of (s - P_h) and (s - P_h)^2, merged by additions in a
 // fixed order at every level (lane -> wave -> block -> stream): deterministic, no divisions, and
 // no cancellation since P_h lies within the spread of the scores.
+#include <algorithm>
+
 #include "common.cuh"
 #include "tria_internal.h"
 
@@ -135,7 +137,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&ka)[4], const u32x4 *__restric
     const int row = (lane & 15) < valid ? (lane & 15) : 0, g = lane >> 4;
     const u32x4 *p = tile_base + row * 16 + g;   // row = 16 x 16 B; byte 64kb + 16g = word 4kb + g
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) ka[kb] = __builtin_nontemporal_load(p + 4 * kb);
+    for (int kb = 0; kb < 4; ++kb) ka[kb] = p[4 * kb];
 }
 
 // v_permlane32_swap: lanes 32..63 of x trade places with lanes 0..31 of y, so that afterwards
@@ -356,8 +358,10 @@ struct WaveScorer {
         }                                                                                      \
     } while (0)
 
-// ---- tiled path: block = (stream, 1024-key tile); raw scores key-major through the workspace ---
-// raw [streams][N][G]; partial sums per (stream, tile, head): s1, s2, min, max.
+// ---- tiled path: block = (stream, 1024-key tile); raw scores head-major through global memory --
+// raw [streams][G][N] (the workspace, or the caller's raw output directly); partial sums per
+// (stream, tile, head): s1, s2, min, max.
+
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_mfma_tile_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N, int tiles,
@@ -378,13 +382,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_tile_kernel(
     const int ntiles16 = (nkeys + 15) >> 4;
     const u32x4 *kb = k + ((size_t)sid * N + j0) * 16;
     const int nt_w = wid < ntiles16 ? (ntiles16 - wid + 3) >> 2 : 0;
-    // raw scores of this block's keys through a buffer resource sized to them: stores of rows
-    // past the end (ragged last tile) and of heads >= G (offset pushed past the end) are dropped
-    // by the hardware, so every tile issues the same two stores and the key loop has no branches
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(raw + ((size_t)sid * N + j0) * G, 0, nkeys * G * 4, 0x00020000);
-    const int off0 = ha < G ? (jj * G + ha) * 4 : 1 << 30;
-    const int off1 = ha + 2 < G ? (jj * G + ha + 2) * 4 : 1 << 30;
+    // Raw scores go out as they are made, through a buffer resource over this block's part of
+    // the stream's rows: a store with an offset past the range (rows past the end of the tile,
+    // heads >= G) is dropped by the hardware, so every ring step issues the same two stores and
+    // the waits of the ring stay exact.  Each store writes 16 consecutive keys of 4 heads.
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        raw + (size_t)sid * G * N + j0, 0, ((G - 1) * N + nkeys) * 4, 0x00020000);
+    constexpr int kDrop = 0x7fffffff;
     // item i of this wave is tile wid + 4i
     auto issue = [&](u32x4 (&b)[4], int i) {
         const int t = min(wid + 4 * i, ntiles16 - 1);
@@ -394,9 +398,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_tile_kernel(
         const int t = wid + 4 * i;
         float v[2];
         ws.score(b, nkeys - t * 16, v);
-        // the whole offset goes in the vector operand: the range check does not include soffset
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[0]), rsrc, off0 + t * 16 * G * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[1]), rsrc, off1 + t * 16 * G * 4, 0, 0);
+        const int key = t * 16 + jj;
+        const bool in = key < nkeys;
+        const int o0 = (in && ha < G) ? (ha * N + key) * 4 : kDrop;
+        const int o1 = (in && ha + 2 < G) ? ((ha + 2) * N + key) * 4 : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[0]), rsrc, o0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[1]), rsrc, o1, 0, 0);
     };
     if (nt_w > 0) TRIA_RING4(nt_w, issue, compute);
     block_sums_stage(bs, ws.m);
@@ -412,49 +419,93 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_tile_kernel(
     }
 }
 
-// Normalisation of the tiled path: adds the stream's tile partials in order, then F for this
-// block's 1024 keys from the key-major raw scores (and the optional head-major raw output).
+// Per-stream statistics of the tiled path: one block per stream adds the tile partials of each
+// head (wave w takes heads w and w + 4; lane l the tiles l, l + 64, ... in order, then a fixed
+// butterfly) and publishes mean and 1/std per head (zst) and the optional head statistics.
 template <int G>
-__global__ __launch_bounds__(kScoreThreads) void zmax_keymajor_kernel(
-    const float *__restrict__ raw, const double *__restrict__ part, const float *__restrict__ pivot, int N,
-    int tiles, float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats,
-    int *__restrict__ err)
+__global__ __launch_bounds__(kScoreThreads) void tile_stats_kernel(const double *__restrict__ part,
+                                                                   const float *__restrict__ pivot, int N, int tiles,
+                                                                   float *__restrict__ zst, float *__restrict__ stats,
+                                                                   int *__restrict__ err)
 {
-    __shared__ float zmu[G], zinv[G];
-    const int sid = blockIdx.x / tiles;
-    const int tile = blockIdx.x - sid * tiles;
-    if (threadIdx.x < G) {
-        const int h = threadIdx.x;
+    const int sid = blockIdx.x;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int h = wid + 4 * s;
+        if (h >= G) break;
         Sums t2;
         t2.init();
-        for (int tt = 0; tt < tiles; ++tt) {
+        for (int tt = lane; tt < tiles; tt += 64) {
             const double *q = part + (((size_t)sid * tiles + tt) * G + h) * 4;
             Sums u;
             u.s1 = q[0]; u.s2 = q[1]; u.mn = (float)q[2]; u.mx = (float)q[3];
             t2.add(u);
         }
-        if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
-        double mean, sd;
-        finish_moments(t2, (double)pivot[(size_t)sid * G + h], (double)N, mean, sd);
-        zmu[h] = (float)mean;
-        zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
-        if (stats && tile == 0) {
-            stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
-            stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            Sums u;
+            u.s1 = __shfl_xor(t2.s1, o, 64);
+            u.s2 = __shfl_xor(t2.s2, o, 64);
+            u.mn = __shfl_xor(t2.mn, o, 64);
+            u.mx = __shfl_xor(t2.mx, o, 64);
+            t2.add(u);
+        }
+        if (lane == 0) {
+            if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
+            double mean, sd;
+            finish_moments(t2, (double)pivot[(size_t)sid * G + h], (double)N, mean, sd);
+            zst[((size_t)sid * G + h) * 2 + 0] = (float)mean;
+            zst[((size_t)sid * G + h) * 2 + 1] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
+            if (stats) {
+                stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
+                stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
+            }
         }
     }
-    __syncthreads();
-    const int j0 = tile * kTileKeys;
-    const int nkeys = min(kTileKeys, N - j0);
-    for (int j = threadIdx.x; j < nkeys; j += kScoreThreads) {
-        const float *r = raw + ((size_t)sid * N + j0 + j) * G;
-        float z = -INFINITY;
+}
+
+// Final scores of the tiled path: F(j) = max_h (raw_h(j) - mean_h) / std_h over the head-major
+// raw rows; one block per (stream, 4096 keys), four keys per thread and step.
+constexpr int kZmaxKeys = 4096;
+
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void zmax_tiles_kernel(const float *__restrict__ raw,
+                                                                   const float *__restrict__ zst, int N, int chunks,
+                                                                   float *__restrict__ F)
+{
+    const int sid = blockIdx.x / chunks;
+    const int c = blockIdx.x - sid * chunks;
+    float mu[G], inv[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) z = fmaxf(z, (r[h] - zmu[h]) * zinv[h]);
-        F[(size_t)sid * N + j0 + j] = z;
-        if (raw_out)
+    for (int h = 0; h < G; ++h) {
+        mu[h] = zst[((size_t)sid * G + h) * 2 + 0];
+        inv[h] = zst[((size_t)sid * G + h) * 2 + 1];
+    }
+    const int j0 = c * kZmaxKeys;
+    const int nk = min(kZmaxKeys, N - j0);
+    const float *r = raw + (size_t)sid * G * N + j0;
+    float *fo = F + (size_t)sid * N + j0;
+    if ((N & 3) == 0 && ((uintptr_t)raw & 15) == 0 && ((uintptr_t)F & 15) == 0) {
+        for (int q = threadIdx.x; q < (nk >> 2); q += kScoreThreads) {
+            float4 z = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
 #pragma unroll
-            for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + j0 + j] = r[h];
+            for (int h = 0; h < G; ++h) {
+                const float4 x = *(const float4 *)(r + (size_t)h * N + 4 * q);
+                z.x = fmaxf(z.x, (x.x - mu[h]) * inv[h]);
+                z.y = fmaxf(z.y, (x.y - mu[h]) * inv[h]);
+                z.z = fmaxf(z.z, (x.z - mu[h]) * inv[h]);
+                z.w = fmaxf(z.w, (x.w - mu[h]) * inv[h]);
+            }
+            *(float4 *)(fo + 4 * q) = z;
+        }
+    } else {
+        for (int j = threadIdx.x; j < nk; j += kScoreThreads) {
+            float z = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < G; ++h) z = fmaxf(z, (r[(size_t)h * N + j] - mu[h]) * inv[h]);
+            fo[j] = z;
+        }
     }
 }
 
@@ -547,15 +598,20 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
         score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
-    float *raw = (float *)(ws + lay.raw_off);
+    // raw scores go straight into the caller's raw output when there is one (same layout)
+    float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
     const long long blocks = (long long)streams * lay.tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     score_mfma_tile_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(kp, ops, pivot, N, lay.tiles, raw, part);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    zmax_keymajor_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(raw, part, pivot, N, lay.tiles, F, raw_out,
-                                                                        stats, err);
+    float *zst = (float *)(ws + lay.zst_off);
+    tile_stats_kernel<G><<<streams, kScoreThreads, 0, st>>>(part, pivot, N, lay.tiles, zst, stats, err);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int chunks = (N + kZmaxKeys - 1) / kZmaxKeys;
+    zmax_tiles_kernel<G><<<(unsigned)((long long)streams * chunks), kScoreThreads, 0, st>>>(raw, zst, N, chunks, F);
     return hipGetLastError();
 }
 

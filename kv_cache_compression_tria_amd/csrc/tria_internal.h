@@ -27,7 +27,7 @@ struct tria_calib {
 
 // Workspace layout of tria_score (every region 256-byte aligned).
 struct tria_score_ws {
-    size_t qrot_off, raw_off, part_off, err_off, ops_off, pivot_off, total;
+    size_t qrot_off, raw_off, part_off, zst_off, err_off, ops_off, pivot_off, total;
     int tiled;       // 1: the stream does not fit one block's LDS
     int tiles;       // key tiles (blocks) per stream on the tiled path
 };
@@ -38,7 +38,8 @@ constexpr int kTileKeys = 1024;       // keys per block on the tiled scoring pat
 constexpr int kScoreThreads = 256;
 constexpr int kFusedLdsMax = 80 * 1024;   // raw scores of a stream kept on chip up to this size
 constexpr int kSelectThreads = 1024;
-constexpr int kSelectLdsKeys = 36864;     // streams up to this many keys are selected from LDS
+constexpr int kSelectLdsKeys = 34560;     // streams up to this many keys are selected from LDS (with 24 KB of
+                                          // static LDS: within the 160 KB of a CU)
 constexpr int kCompactThreads = 256;
 constexpr int kCompactRows = 64;
 
