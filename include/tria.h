@@ -147,6 +147,26 @@ tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void 
 
 const char *tria_status_string(tria_status status);
 
+/*
+ * Kernel timing (instrumentation, off by default).  While enabled, every timed kernel launched by
+ * tria_score, tria_select_topB, tria_compact and tria_prune is bracketed by a pair of HIP events
+ * recorded on the stream it runs on.  tria_timing_read waits for the recorded events, returns the
+ * summed elapsed milliseconds and the number of timed launches per timer, and starts a new
+ * accumulation.  Recording creates HIP events (a runtime allocation) the first time a pair is
+ * needed: keep timing off where nothing may allocate.  Errors: INVALID (NULL outputs), DEVICE
+ * (an event could not be read; the other sums are still returned).
+ */
+typedef enum {
+    TRIA_TIMER_SCORE_KEYS = 0, /* the kernel that reads every cached key and scores it */
+    TRIA_TIMER_NORMALISE = 1,  /* per-head statistics, z-score and GQA max (long streams) */
+    TRIA_TIMER_SELECT = 2,     /* top-B selection */
+    TRIA_TIMER_COMPACT = 3,    /* in-place compaction */
+    TRIA_TIMER_COUNT = 4
+} tria_timer;
+
+tria_status tria_timing_enable(int on);
+tria_status tria_timing_read(double *ms /* [TRIA_TIMER_COUNT] */, int *launches /* [TRIA_TIMER_COUNT] */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,8 +26,9 @@ KEYS_PRE_ROPE = 2
 EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
-    "tria_prune_workspace_bytes", "tria_prune", "tria_status_string",
+    "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
 )
+TIMERS = ("score_keys", "normalise", "select", "compact")
 
 
 class TriaError(RuntimeError):
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.tria_prune.argtypes = [P, I, P, P, P, P, I, I, I, P, P, U, P, S, P]
         L.tria_status_string.restype = ctypes.c_char_p
         L.tria_status_string.argtypes = [I]
+        L.tria_timing_enable.restype = I
+        L.tria_timing_enable.argtypes = [I]
+        L.tria_timing_read.restype = I
+        L.tria_timing_read.argtypes = [ctypes.POINTER(D), ctypes.POINTER(I)]
         _lib = L
     return _lib
 
@@ -258,3 +263,17 @@ def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int
                           _stream(stream))
     _check(st, "tria_prune")
     return F, kept
+
+
+def timing_enable(on: bool = True):
+    """Turn per-kernel event timing on or off (``tria_timing_enable``)."""
+    _check(lib().tria_timing_enable(1 if on else 0), "tria_timing_enable")
+
+
+def timing_read() -> dict:
+    """Summed milliseconds and launch counts per timed kernel since the last read
+    (``tria_timing_read``); waits for the recorded events."""
+    ms = (ctypes.c_double * len(TIMERS))()
+    n = (ctypes.c_int * len(TIMERS))()
+    _check(lib().tria_timing_read(ms, n), "tria_timing_read")
+    return {name: {"ms": ms[i], "launches": n[i]} for i, name in enumerate(TIMERS)}

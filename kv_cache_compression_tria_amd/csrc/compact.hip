@@ -76,6 +76,7 @@ hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const i
                           int N, int B, hipStream_t st)
 {
     const int nk = B < N ? B : N;
+    KernelTimer timer(TRIA_TIMER_COMPACT, st);
     if (dt == TRIA_BF16)
         compact_kernel<16><<<n_streams, kCompactThreads, 0, st>>>((uint4 *)k, (uint4 *)v, pos, kept, N, nk);
     else

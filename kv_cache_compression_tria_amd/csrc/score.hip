@@ -444,6 +444,7 @@ static hipError_t launch_score_t(const tria_calib *c, const void *k, int n_seq, 
             if (e != hipSuccess) return e;
             attr_set = true;
         }
+        KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
         score_fused_kernel<BF16, G><<<streams, kScoreThreads, lds, st>>>(
             (const uint4 *)k, qrot, c->W, c->L, c->Hkv, N, F, raw_out, stats, err);
         return hipGetLastError();
@@ -452,10 +453,15 @@ static hipError_t launch_score_t(const tria_calib *c, const void *k, int n_seq, 
     double *part = (double *)(ws + lay.part_off);
     const long long blocks = (long long)streams * lay.tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    score_tile_kernel<BF16, G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(
-        (const uint4 *)k, qrot, c->W, c->L, c->Hkv, N, lay.tiles, raw, part, err);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    {
+        KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
+        score_tile_kernel<BF16, G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(
+            (const uint4 *)k, qrot, c->W, c->L, c->Hkv, N, lay.tiles, raw, part, err);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
+    KernelTimer timer(TRIA_TIMER_NORMALISE, st);
     return launch_zmax(G, raw, part, streams, N, lay.tiles, F, stats, st);
 }
 

@@ -595,6 +595,7 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
             if (e != hipSuccess) return e;
             attr_set = true;
         }
+        KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
         score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
@@ -603,9 +604,13 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
     double *part = (double *)(ws + lay.part_off);
     const long long blocks = (long long)streams * lay.tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    score_mfma_tile_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(kp, ops, pivot, N, lay.tiles, raw, part);
-    e = hipGetLastError();
+    {
+        KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
+        score_mfma_tile_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(kp, ops, pivot, N, lay.tiles, raw, part);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
+    KernelTimer timer(TRIA_TIMER_NORMALISE, st);
     float *zst = (float *)(ws + lay.zst_off);
     tile_stats_kernel<G><<<streams, kScoreThreads, 0, st>>>(part, pivot, N, lay.tiles, zst, stats, err);
     e = hipGetLastError();

@@ -235,6 +235,7 @@ __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N
 
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st)
 {
+    KernelTimer timer(TRIA_TIMER_SELECT, st);
     if (B >= N) {
         const size_t n = (size_t)n_streams * N;
         identity_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(kept, n_streams, N);

@@ -45,6 +45,21 @@ constexpr int kCompactRows = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Brackets the kernel launches of its scope with a HIP event pair on `st` when timing is enabled
+// (tria_timing_enable); does nothing otherwise.
+class KernelTimer {
+  public:
+    KernelTimer(int which, hipStream_t st);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer &) = delete;
+    KernelTimer &operator=(const KernelTimer &) = delete;
+
+  private:
+    int which_;
+    hipStream_t st_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
 tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys);
 
 // kernel launchers (return hipSuccess or the launch error)

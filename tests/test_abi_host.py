@@ -104,3 +104,17 @@ def test_score_select_compact_validation(tria):
     # B >= N is the identity: nothing to launch
     assert L.tria_compact(0, fake, fake, None, fake, 1, 16, 16, 128, None) == tria.OK
     assert L.tria_prune(None, 0, fake, fake, None, fake, 1, 16, 4, fake, fake, 0, fake, 1 << 20, None) == tria.E_INVALID
+
+
+def test_timing_api_without_pending_events(tria):
+    """Timing can be switched on and off and read with nothing recorded (no GPU needed)."""
+    T = tria
+    L = T.lib()
+    ms = (ctypes.c_double * 4)()
+    n = (ctypes.c_int * 4)()
+    assert L.tria_timing_enable(1) == T.OK
+    assert L.tria_timing_read(ms, n) == T.OK
+    assert list(n) == [0, 0, 0, 0] and list(ms) == [0.0, 0.0, 0.0, 0.0]
+    assert L.tria_timing_enable(0) == T.OK
+    assert L.tria_timing_read(None, n) == T.E_INVALID
+    assert T.timing_read() == {name: {"ms": 0.0, "launches": 0} for name in T.TIMERS}
