@@ -11,9 +11,11 @@
 //      onto few bins: each wave first counts its heavy bins with one ballot per bin and a single
 //      atomic, and only the scattered rest use per-lane atomics;
 //   3. wave w owns the contiguous key range [w*N/16, (w+1)*N/16): it counts its keys > T and
-//      == T, one scan over the 16 wave totals gives its output base, and it writes every index
+//      == T, a prefix over the 16 wave totals gives its output base, and it writes every index
 //      with key > T and the first k indices with key == T (in index order) at
 //      slot = #(key > T before j) + min(#(key == T before j), k).
+//   The candidate list of step 2 is written the same way (count, prefix, write): no atomics,
+//   and the candidates keep index order.
 #include "common.cuh"
 #include "tria_internal.h"
 
@@ -48,6 +50,12 @@ constexpr int kBins0 = 2048;      // digit 0: the top 11 bits of the order key
 constexpr int kCand = 4096;       // candidate list (keys of the chosen digit-0 bin), in LDS
 static_assert(kSelectLdsKeys * 4 + (kBins0 + kCand) * 4 + 512 <= 160 * 1024, "select LDS exceeds a CU's 160 KB");
 
+// Exclusive prefix over the lanes of a 64-bit ballot mask: the number of set lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <bool IN_LDS>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__restrict__ F, int N, int B,
                                                                 int32_t *__restrict__ kept)
@@ -57,11 +65,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
     extern __shared__ uint32_t keys[];                // [N] when IN_LDS
     __shared__ uint32_t hist[kBins0];
     __shared__ uint32_t cand[kCand];
-    __shared__ uint32_t wgt[NW], weq[NW];
-    __shared__ uint32_t s_prefix, s_k, s_ncand;
+    __shared__ uint32_t wa[NW], wb[NW];
+    __shared__ uint32_t s_prefix, s_k;
 
     const int sid = blockIdx.x;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform loop bounds
     const float *f = F + (size_t)sid * N;
     int32_t *out = kept + (size_t)sid * B;            // B < N on this path
     if (IN_LDS) {
@@ -102,6 +111,33 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
         __syncthreads();
     }
     auto key_at = [&](int j) -> uint32_t { return IN_LDS ? keys[j] : order_key(f[j]); };
+    // wave w owns the contiguous key range [lo, hi); it walks it 256 keys per step, lane l taking
+    // keys b + 64e + l (e < 4): four independent reads per step, visited in index order
+    const int per = (N + NW - 1) / NW;
+    const int lo = min(N, wid * per), hi = min(N, lo + per);
+    auto load4 = [&](int b, uint32_t (&u)[4], bool (&in)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = b + 64 * e + lane;
+            in[e] = j < hi;
+            u[e] = in[e] ? key_at(j) : 0u;
+        }
+    };
+    // exclusive prefix over the waves of per-wave totals (a, b), via LDS
+    auto wave_prefix = [&](uint32_t a, uint32_t b, uint32_t &pa, uint32_t &pb) {
+        if (lane == 0) {
+            wa[wid] = a;
+            wb[wid] = b;
+        }
+        __syncthreads();
+        pa = 0u;
+        pb = 0u;
+        for (int w = 0; w < wid; ++w) {
+            pa += wa[w];
+            pb += wb[w];
+        }
+        __syncthreads();
+    };
 
     // digit 0 = bits 31..21 over every key; the keys of the chosen digit-0 bin are then copied
     // to a candidate list (when they fit) and digits 1 (bits 20..10) and 2 (bits 9..0) are
@@ -112,14 +148,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
         if (wid == 0) {
             // lane l owns bins nbins-1-l*per .. nbins-per-l*per (descending); find the bin where
             // the count of larger-or-equal keys first reaches k
-            const int per = nbins / 64;
+            const int per_lane = nbins / 64;
             uint32_t local = 0u;
-            for (int i = 0; i < per; ++i) local += hist[nbins - 1 - lane * per - i];
+            for (int i = 0; i < per_lane; ++i) local += hist[nbins - 1 - lane * per_lane - i];
             const uint32_t incl = wave_incl_scan(local);
             uint32_t excl = incl - local;
             if (excl < k && k <= incl) {
-                for (int i = 0; i < per; ++i) {
-                    const int bin = nbins - 1 - lane * per - i;
+                for (int i = 0; i < per_lane; ++i) {
+                    const int bin = nbins - 1 - lane * per_lane - i;
                     const uint32_t c = hist[bin];
                     if (excl + c >= k) {
                         s_prefix = prefix | ((uint32_t)bin << shift);
@@ -140,33 +176,46 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
     };
 
     clear_hist(kBins0);
-    for (int base = 0; base < N; base += NT) {       // uniform trip count: ballots see the whole wave
-        const int j = base + threadIdx.x;
-        const uint32_t u = j < N ? key_at(j) : 0u;
-        hist_add(hist, u >> 21, j < N);
+    for (int b = lo; b < hi; b += 256) {
+        uint32_t u[4];
+        bool in[4];
+        load4(b, u, in);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hist_add(hist, u[e] >> 21, in[e]);
     }
     find_bin(21, kBins0);
     mask = 0xffe00000u;
 
-    // candidates: keys whose digit 0 matches
-    if (threadIdx.x == 0) s_ncand = 0u;
-    __syncthreads();
-    const bool listed = hist[prefix >> 21] <= (uint32_t)kCand;   // read before the histogram is reused
+    // candidates (keys whose digit 0 matches), written in index order without atomics: count per
+    // wave, prefix over the waves, then write
+    const bool listed = hist[prefix >> 21] <= (uint32_t)kCand;   // uniform; read before hist is reused
+    int ncand = 0;
     if (listed) {
-        for (int base = 0; base < N; base += NT) {
-            const int j = base + threadIdx.x;
-            const uint32_t u = j < N ? key_at(j) : 0u;
-            const bool m = j < N && (u & mask) == prefix;
-            const uint64_t bal = __ballot(m);
-            uint32_t wbase = 0u;
-            if (lane == 0 && bal) wbase = atomicAdd(&s_ncand, (uint32_t)__builtin_popcountll(bal));
-            wbase = __builtin_amdgcn_readfirstlane(wbase);
-            if (m)
-                cand[wbase + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = u;
+        uint32_t c = 0u;
+        for (int b = lo; b < hi; b += 256) {
+            uint32_t u[4];
+            bool in[4];
+            load4(b, u, in);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c += __builtin_popcountll(__ballot(in[e] && (u[e] & mask) == prefix));
         }
+        uint32_t run, unused;
+        wave_prefix(c, 0u, run, unused);
+        for (int b = lo; b < hi; b += 256) {
+            uint32_t u[4];
+            bool in[4];
+            load4(b, u, in);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool m = in[e] && (u[e] & mask) == prefix;
+                const uint64_t bal = __ballot(m);
+                if (m) cand[run + lanes_below(bal)] = u[e];
+                run += __builtin_popcountll(bal);
+            }
+        }
+        ncand = (int)hist[prefix >> 21];
+        __syncthreads();
     }
-    __syncthreads();
-    const int ncand = (int)s_ncand;
     for (int d = 1; d <= 2; ++d) {
         const int shift = d == 1 ? 10 : 0;
         const int nbins = d == 1 ? 2048 : 1024;
@@ -178,10 +227,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
                 hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), i < ncand && (u & mask) == prefix);
             }
         } else {
-            for (int base = 0; base < N; base += NT) {
-                const int j = base + threadIdx.x;
-                const uint32_t u = j < N ? key_at(j) : 0u;
-                hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), j < N && (u & mask) == prefix);
+            for (int b = lo; b < hi; b += 256) {
+                uint32_t u[4];
+                bool in[4];
+                load4(b, u, in);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hist_add(hist, (u[e] >> shift) & (uint32_t)(nbins - 1), in[e] && (u[e] & mask) == prefix);
             }
         }
         find_bin(shift, nbins);
@@ -189,41 +241,35 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
     }
     const uint32_t T = prefix;   // the B-th largest key; k of the keys equal to T are kept
 
-    // ordered write: wave w walks its contiguous range in 64-key steps
-    const int per = (N + NW - 1) / NW;
-    const int lo = min(N, wid * per), hi = min(N, lo + per);
+    // ordered write: count each wave's keys > T and == T, prefix over the waves, then write
     uint32_t ngt = 0u, neq = 0u;
-    for (int b = lo; b < hi; b += 64) {
-        const int j = b + lane;
-        const uint32_t u = j < hi ? key_at(j) : 0u;
-        ngt += __builtin_popcountll(__ballot(j < hi && u > T));
-        neq += __builtin_popcountll(__ballot(j < hi && u == T));
+    for (int b = lo; b < hi; b += 256) {
+        uint32_t u[4];
+        bool in[4];
+        load4(b, u, in);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ngt += __builtin_popcountll(__ballot(in[e] && u[e] > T));
+            neq += __builtin_popcountll(__ballot(in[e] && u[e] == T));
+        }
     }
-    if (lane == 0) {
-        wgt[wid] = ngt;
-        weq[wid] = neq;
-    }
-    __syncthreads();
-    uint32_t gt_run = 0u, eq_run = 0u;
-    for (int w = 0; w < wid; ++w) {
-        gt_run += wgt[w];
-        eq_run += weq[w];
-    }
-    for (int b = lo; b < hi; b += 64) {
-        const int j = b + lane;
-        const uint32_t u = j < hi ? key_at(j) : 0u;
-        const bool gt = j < hi && u > T, eq = j < hi && u == T;
-        const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
-        const uint32_t gt_before = gt_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mgt >> 32),
-                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mgt, 0u));
-        const uint32_t eq_before = eq_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(meq >> 32),
-                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)meq, 0u));
-        uint32_t slot = 0xffffffffu;
-        if (gt) slot = gt_before + min(eq_before, k);
-        else if (eq && eq_before < k) slot = gt_before + eq_before;
-        if (slot < (uint32_t)B) out[slot] = j;      // always true for a valid histogram walk
-        gt_run += __builtin_popcountll(mgt);
-        eq_run += __builtin_popcountll(meq);
+    uint32_t gt_run, eq_run;
+    wave_prefix(ngt, neq, gt_run, eq_run);
+    for (int b = lo; b < hi; b += 256) {
+        uint32_t u[4];
+        bool in[4];
+        load4(b, u, in);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool gt = in[e] && u[e] > T, eq = in[e] && u[e] == T;
+            const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
+            const uint32_t gb = gt_run + lanes_below(mgt), eb = eq_run + lanes_below(meq);
+            // every key > T is kept, and the first k keys == T; slot = keys kept before this one
+            const uint32_t slot = gt ? gb + min(eb, k) : ((eq && eb < k) ? gb + eb : 0xffffffffu);
+            if (slot < (uint32_t)B) out[slot] = b + 64 * e + lane;   // always true for a kept key
+            gt_run += __builtin_popcountll(mgt);
+            eq_run += __builtin_popcountll(meq);
+        }
     }
 }
 
