@@ -44,7 +44,7 @@ def lib():
         L.oracle_omega.restype = D
         L.oracle_omega.argtypes = [D, I, I]
         L.oracle_score_stream.restype = None
-        L.oracle_score_stream.argtypes = [I, I, I, I, P, P, ctypes.c_int64, P, P, P, D, P, I, I, P, P, P]
+        L.oracle_score_stream.argtypes = [I, I, I, I, P, P, ctypes.c_int64, P, P, P, D, P, I, I, I, P, P, P]
         L.oracle_zmax.restype = I
         L.oracle_zmax.argtypes = [I, I, P, P, P, P, P]
         L.oracle_select.restype = I
@@ -52,7 +52,7 @@ def lib():
         L.oracle_compact_rows.restype = None
         L.oracle_compact_rows.argtypes = [I, ctypes.c_size_t, P, P]
         L.oracle_prune_streams.restype = I
-        L.oracle_prune_streams.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, D, P, I, I,
+        L.oracle_prune_streams.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, D, P, I, I,
                                            P, I, P, P, P, I]
         L.oracle_max_threads.restype = I
         L.oracle_max_threads.argtypes = [I]
@@ -76,10 +76,11 @@ def omega(theta: float, f: int, d: int) -> float:
     return lib().oracle_omega(theta, f, d)
 
 
-def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, form="lit"):
+def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, form="lit", pre_rope=False):
     """Raw scores of one stream.
 
-    keys [N][d] (uint16 bf16 bits or float32, post-RoPE), pos [N] int32, t int,
+    keys [N][d] (uint16 bf16 bits or float32; post-RoPE, or pre-RoPE with ``pre_rope``),
+    pos [N] int32, t int,
     qc [G][d], qn [G][d/2], rb [G][d/2] float32.
     Returns (s_trig, s_norm, raw), each float64 [G][N].
     """
@@ -96,7 +97,7 @@ def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, f
     raw = np.zeros((G, N))
     lib().oracle_score_stream(N, d, G, _keys_dtype(keys), _ptr(keys), _ptr(pos), int(t), _ptr(qc),
                               _ptr(qn), _ptr(rb), float(theta), _ptr(off), len(off),
-                              0 if form == "lit" else 1, _ptr(st), _ptr(sn), _ptr(raw))
+                              0 if form == "lit" else 1, int(bool(pre_rope)), _ptr(st), _ptr(sn), _ptr(raw))
     return st, sn, raw
 
 
@@ -135,10 +136,11 @@ def compact_rows(rows: np.ndarray, kept: np.ndarray) -> np.ndarray:
 
 
 def prune_streams(keys, pos, t, qc, qn, rb, B, n_kv_heads, stream_ids=None, theta=1e6,
-                  offsets=DEFAULT_OFFSETS, form="fac", want_raw=False, n_threads=0):
+                  offsets=DEFAULT_OFFSETS, form="fac", want_raw=False, n_threads=0, pre_rope=False):
     """Oracle prune over a list of streams.
 
     keys [n][N][d] and pos [n][N] hold the listed streams (packed, in ``stream_ids`` order);
+    keys are post-RoPE, or the pre-RoPE bands themselves with ``pre_rope``;
     ``stream_ids`` are the global ids (s*L + l)*Hkv + g (default: 0..n-1).
     t [S], qc [L][Hq][d], qn/rb [L][Hq][d/2].
     Returns dict with F [n][N], kept [n][min(B,N)] and (optionally) raw [n][G][N].
@@ -167,7 +169,7 @@ def prune_streams(keys, pos, t, qc, qn, rb, B, n_kv_heads, stream_ids=None, thet
     qn_ = np.ascontiguousarray(qn, dtype=np.float32)
     rb_ = np.ascontiguousarray(rb, dtype=np.float32)
     off = np.ascontiguousarray(offsets, dtype=np.int64)
-    rc = lib().oracle_prune_streams(0 if form == "lit" else 1, _keys_dtype(keys), S, L, Hkv, G, N, d,
+    rc = lib().oracle_prune_streams(0 if form == "lit" else 1, int(bool(pre_rope)), _keys_dtype(keys), S, L, Hkv, G, N, d,
                                     _ptr(keys), _ptr(pp), _ptr(tt), _ptr(qc_), _ptr(qn_), _ptr(rb_),
                                     float(theta), _ptr(off), len(off), int(B), _ptr(ids), n,
                                     _ptr(F), _ptr(raw), _ptr(kept), int(n_threads))

@@ -20,7 +20,8 @@
  *    ([p3] section "技术细节补充 / RoPE回顾"; [p1] section 1.3).
  *    w_f = fl32(theta^(-2f/d)): the fp64 power rounded once to fp32, then used exactly.
  *  - Cached keys are post-RoPE.  The pre-RoPE key band is recovered as
- *    k_f = ktilde_f * exp(-i*w_f*p_j).
+ *    k_f = ktilde_f * exp(-i*w_f*p_j).  A cache that stores keys before RoPE (the layout the
+ *    library serves with a flag) gives k_f directly; the score is the same function of k_f.
  *  - Trigonometric score ([p3] section "TriAttention：把理论变成算法" item 1, [p1] section 3.1):
  *      S_trig(j) = mean over d in D of sum_f |qbar_f| |k_f| cos(w_f*(t+d-p_j) + arg qbar_f - arg k_f)
  *    with the future-offset set D = {1, 2, 4, ..., 2^16} ([p1] section 3.3).  The offsets are
@@ -87,11 +88,12 @@ static double load_elem(const void *base, int dtype, size_t idx)
  *   rb     : [G][d/2]  R_f
  *   off    : [n_off]   future offsets D
  *   form   : 0 = lit, 1 = fac
+ *   pre_rope: 0 = keys are post-RoPE (ktilde), 1 = keys are the pre-RoPE bands k_f themselves
  * Outputs (each [G][N], any may be NULL): s_trig, s_norm, raw = s_trig + s_norm.
  */
 void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const int32_t *pos,
                          int64_t t, const float *qc, const float *qn, const float *rb,
-                         double theta, const int64_t *off, int n_off, int form,
+                         double theta, const int64_t *off, int n_off, int form, int pre_rope,
                          double *s_trig, double *s_norm, double *raw)
 {
     const int half = d / 2;
@@ -113,10 +115,13 @@ void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const
         for (int f = 0; f < half; ++f) {
             double x = load_elem(keys, dtype, (size_t)j * d + f);
             double y = load_elem(keys, dtype, (size_t)j * d + f + half);
-            double a = w[f] * p;                 /* exact: 24-bit w times |p| < 2^31 */
-            double ca = cos(a), sa = sin(a);
-            double kr = x * ca + y * sa;         /* (x + i y) * exp(-i a) */
-            double ki = y * ca - x * sa;
+            double kr = x, ki = y;
+            if (!pre_rope) {
+                double a = w[f] * p;             /* exact: 24-bit w times |p| < 2^31 */
+                double ca = cos(a), sa = sin(a);
+                kr = x * ca + y * sa;            /* (x + i y) * exp(-i a) */
+                ki = y * ca - x * sa;
+            }
             kmag[f] = sqrt(kr * kr + ki * ki);
             karg[f] = atan2(ki, kr);
         }
@@ -248,7 +253,7 @@ void oracle_compact_rows(int nk, size_t row_bytes, unsigned char *rows, const in
  * kept_out [n_idx][min(B,N)] (may be NULL).
  * Returns 0, or -1 if a non-finite score was met.
  */
-int oracle_prune_streams(int form, int dtype, int S, int L, int Hkv, int G, int N, int d,
+int oracle_prune_streams(int form, int pre_rope, int dtype, int S, int L, int Hkv, int G, int N, int d,
                          const void *keys, const int32_t *pos, const int64_t *t,
                          const float *qc, const float *qn, const float *rb, double theta,
                          const int64_t *off, int n_off, int B,
@@ -276,7 +281,7 @@ int oracle_prune_streams(int form, int dtype, int S, int L, int Hkv, int G, int 
         double *raw = raw_out ? raw_out + (size_t)i * G * N : (double *)malloc(sizeof(double) * (size_t)G * N);
         double *F = F_out ? F_out + (size_t)i * N : (double *)malloc(sizeof(double) * (size_t)N);
         oracle_score_stream(N, d, G, dtype, kb, pb, t[s], qc + h0 * d, qn + h0 * half, rb + h0 * half,
-                            theta, off, n_off, form, NULL, NULL, raw);
+                            theta, off, n_off, form, pre_rope, NULL, NULL, raw);
         int rc = oracle_zmax(N, G, raw, NULL, F, NULL, NULL);
         if (rc == 0 && kept_out) rc = oracle_select(N, B, F, kept_out + (size_t)i * nk) < 0 ? -1 : 0;
         if (rc != 0) bad |= 1;

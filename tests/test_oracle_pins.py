@@ -196,6 +196,68 @@ def test_p10_fac_equals_lit(orc):
         assert np.max(np.abs(x - y)) <= 1e-12 * np.max(np.abs(x))
 
 
+# ---- P11: keys cached before RoPE ---------------------------------------------------------------
+
+@pytest.mark.parametrize("form", ["lit", "fac"])
+def test_p11_pre_rope_keys_zero_offset_is_rope_dot(orc, form):
+    """Pre-RoPE keys, D = {0}: the score is <RoPE(qbar, t), RoPE(k_j, p_j)>, both rotations done
+    here with numpy (the trig series depends on the key only through its pre-RoPE bands)."""
+    rng = np.random.default_rng(111)
+    d, G, N, t = 128, 3, 16, 20000
+    w = synth.omega_table(d)
+    pre = rng.standard_normal((N, d)).astype(np.float32)
+    pos = rng.integers(0, t + 1, N).astype(np.int32)
+    qc = rng.standard_normal((G, d)).astype(np.float32)
+    ones = np.ones((G, d // 2), np.float32)
+    st, _, _ = orc.score_stream(pre, pos, t, qc, ones, ones, offsets=(0,), form=form, pre_rope=True)
+    expect = np_rope(qc.astype(np.float64), t, w) @ np_rope(pre.astype(np.float64), pos, w).T
+    # angles reach 2e4 rad (band 0 has w = 1): each fp64 cos/sin of them is good to ~4e-12, and
+    # 64 bands of |q||k| ~ 1 add up to a few 1e-11
+    np.testing.assert_allclose(st, expect, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_p11_pre_rope_equals_post_rope_of_same_keys(orc, dtype):
+    """The same pre-RoPE keys scored directly and after a RoPE done here (fp64, rounded to fp32):
+    every score agrees to the rounding of the stored post-RoPE keys (relative 1e-6), and the
+    norm scores agree too (|k_f| is RoPE-invariant)."""
+    rng = np.random.default_rng(112)
+    d, G, N, t = 128, 4, 60, 30000
+    w = synth.omega_table(d)
+    pre32 = (1.5 * rng.standard_normal(d) + rng.standard_normal((N, d))).astype(np.float32)
+    keys = pre32 if dtype == "f32" else synth.f32_to_bf16_bits(pre32)
+    pos = np.sort(rng.choice(t + 1, size=N, replace=False)).astype(np.int32)
+    post = np_rope(keys_f64(keys), pos, w).astype(np.float32)
+    qc = (8 * rng.standard_normal((G, d)) / math.sqrt(d)).astype(np.float32)
+    qn = rng.uniform(0.5, 2.0, (G, d // 2)).astype(np.float32)
+    rb = rng.uniform(0.6, 0.99, (G, d // 2)).astype(np.float32)
+    a = orc.score_stream(keys, pos, t, qc, qn, rb, form="fac", pre_rope=True)
+    b = orc.score_stream(post, pos, t, qc, qn, rb, form="fac")
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) <= 1e-6 * np.max(np.abs(x))
+
+
+def test_p11_pre_rope_single_band_closed_form(orc):
+    """Pre-RoPE keys, one band: S = |q_f||k_f| mean_d cos(w_f (t+d-p) + arg q - arg k) with k
+    taken as stored (no phase recovery), worked with cmath."""
+    d, t, f = 128, 4000, 9
+    w = synth.omega_table(d)
+    qc = np.zeros((1, d), np.float32)
+    qc[0, f], qc[0, f + 64] = -0.5, 2.0
+    pre = np.zeros((2, d), np.float32)
+    pre[:, f] = [1.25, -3.0]
+    pre[:, f + 64] = [0.5, 0.75]
+    pos = np.array([17, 3998], np.int32)
+    ones = np.ones((1, 64), np.float32)
+    st, _, _ = orc.score_stream(pre, pos, t, qc, ones, ones, form="lit", pre_rope=True)
+    q = complex(-0.5, 2.0)
+    for j in range(2):
+        k = complex(float(pre[j, f]), float(pre[j, f + 64]))
+        val = sum(abs(q) * abs(k) * math.cos(w[f] * (t + dd - int(pos[j])) + math.atan2(q.imag, q.real)
+                                             - math.atan2(k.imag, k.real)) for dd in D_DEF) / len(D_DEF)
+        assert abs(st[0, j] - val) < 1e-12 * abs(q) * abs(k)
+
+
 # ---- z-score and GQA max ------------------------------------------------------------------------
 
 def test_zscore_moments_and_max(orc):
