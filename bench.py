@@ -60,6 +60,9 @@ def measured_traffic() -> dict:
     return out
 
 
+VARIANTS = ("default", "per_key_phase", "pre_rope")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,6 +72,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--variant", choices=VARIANTS, default="default",
+                    help="scoring form: default (post-RoPE keys, rotated queries), per_key_phase (post-RoPE "
+                         "keys, literal per-key phases), pre_rope (keys cached before RoPE)")
     return ap.parse_args()
 
 
@@ -101,10 +107,12 @@ def main():
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     t0 = time.time()
+    pre_rope = args.variant == "pre_rope"
+    flags = {"default": 0, "per_key_phase": T.PER_KEY_PHASE, "pre_rope": T.KEYS_PRE_ROPE}[args.variant]
     if args.config >= 4:
-        wl = synth.make_device(cfg, dev)
+        wl = synth.make_device(cfg, dev, pre_rope=pre_rope)
     else:
-        wl = synth.to_device(synth.make_host(cfg), dev)
+        wl = synth.to_device(synth.make_host(cfg, pre_rope=pre_rope), dev)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     # The generated tensors stay as the pristine copy; the timed cache is a fresh allocation made
@@ -133,7 +141,7 @@ def main():
 
     def step():
         ev[0].record(stream)
-        T.score(calib, k, t, F=F, ws=ws, stream=stream)
+        T.score(calib, k, t, F=F, ws=ws, stream=stream, pos=pos if flags else None, flags=flags)
         ev[1].record(stream)
         T.select_topB(F, B, kept=kept, stream=stream)
         ev[2].record(stream)
@@ -203,7 +211,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "streams": n_streams, "keys_per_stream": N, "budget": B,
                    "layers": L, "seqs": S, "q_heads": cfg.n_q_heads, "kv_heads": Hkv, "head_dim": d,
-                   "cache_dtype": cfg.dtype, "parallelism": "single-gpu"},
+                   "cache_dtype": cfg.dtype, "score_variant": args.variant, "parallelism": "single-gpu"},
         "alg_bytes_per_step": int(alg),
         "alg_GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -218,12 +226,12 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3))
+        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3), pre_rope)
     calib.free()
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s):
+def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False):
     """The fp64 oracle (factored form, OpenMP over streams) on a bounded sample of streams of the
     same workload, timed on the host cores."""
     import synth
@@ -240,7 +248,7 @@ def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s):
         ph = pp[ids[0]:ids[-1] + 1].cpu().numpy()
         t0 = time.perf_counter()
         oracle.prune_streams(kh, ph, wl["t"], wl["qc"], wl["qn"], wl["rb"], cfg.budget, cfg.n_kv_heads,
-                             stream_ids=ids, form="fac", n_threads=threads)
+                             stream_ids=ids, form="fac", n_threads=threads, pre_rope=pre_rope)
         return time.perf_counter() - t0
 
     n = max(1, min(threads, kk.shape[0]))

@@ -168,9 +168,9 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     if (n_seq <= 0 || N <= 0 || N > (1 << 24)) return TRIA_E_INVALID;
     if ((flags & ~(TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0) return TRIA_E_INVALID;
     if ((flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) && !pos) return TRIA_E_INVALID;
-    if (flags != 0) return TRIA_E_UNSUPPORTED;
     if ((size_t)n_seq * c->L * c->Hkv > (size_t)0x7fffffff) return TRIA_E_INVALID;
-    if (!aligned(k, 16) || !aligned(F, 4) || (raw && !aligned(raw, 4)) || (stats && !aligned(stats, 4)))
+    if (!aligned(k, 16) || !aligned(F, 4) || (raw && !aligned(raw, 4)) || (stats && !aligned(stats, 4)) ||
+        (pos && !aligned(pos, 4)))
         return TRIA_E_INVALID;
     tria_score_ws lay = tria::score_ws_layout(c, dt, n_seq, N);
     if (!ws || ws_bytes < lay.total || !aligned(ws, 256)) return TRIA_E_WORKSPACE;

@@ -43,7 +43,9 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
         w.pivot_off = off;
         off += align256(heads * sizeof(float));
     }
-    if (w.tiled) {
+    {
+        // raw scores, tile partials and per-head mean / 1/std: used by the tiled paths and by the
+        // per-key-phase variants at any length (the workspace size does not depend on the flags)
         w.raw_off = off;
         off += align256(heads * (size_t)N * sizeof(float));
         w.part_off = off;
@@ -487,9 +489,7 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
-    (void)pos;
-    (void)t;
-    if (flags != 0) return hipErrorInvalidValue;   // per-key-phase forms: see the variant kernels
+    if (flags != 0) return launch_score_perkey(c, dt, k, pos, t, n_seq, N, flags, F, raw, stats, lay, ws, st);
     // bf16 caches score on the matrix cores; fp32 caches on the vector ALU
     return dt == TRIA_BF16 ? launch_score_mfma(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st)
                            : launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kScoreThreads) void tile_stats_kernel(const double 
         if (lane == 0) {
             if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
             double mean, sd;
-            finish_moments(t2, (double)pivot[(size_t)sid * G + h], (double)N, mean, sd);
+            finish_moments(t2, pivot ? (double)pivot[(size_t)sid * G + h] : 0.0, (double)N, mean, sd);
             zst[((size_t)sid * G + h) * 2 + 0] = (float)mean;
             zst[((size_t)sid * G + h) * 2 + 1] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
             if (stats) {
@@ -575,6 +575,38 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_fused_kernel(
 
 // ---- launch ------------------------------------------------------------------------------------
 template <int G>
+static hipError_t launch_tile_finish_g(int streams, int N, const float *raw, const double *part, const float *pivot,
+                                       float *F, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+{
+    KernelTimer timer(TRIA_TIMER_NORMALISE, st);
+    int *err = (int *)(ws + lay.err_off);
+    float *zst = (float *)(ws + lay.zst_off);
+    tile_stats_kernel<G><<<streams, kScoreThreads, 0, st>>>(part, pivot, N, lay.tiles, zst, stats, err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long blocks = (long long)streams * ((N + kZmaxKeys - 1) / kZmaxKeys);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    zmax_tiles_kernel<G><<<(unsigned)blocks, kScoreThreads, 0, st>>>(raw, zst, N, (N + kZmaxKeys - 1) / kZmaxKeys, F);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_finish(int G, int streams, int N, const float *raw, const double *part, const float *pivot,
+                              float *F, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+{
+    switch (G) {
+    case 1: return launch_tile_finish_g<1>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 2: return launch_tile_finish_g<2>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 3: return launch_tile_finish_g<3>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 4: return launch_tile_finish_g<4>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 5: return launch_tile_finish_g<5>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 6: return launch_tile_finish_g<6>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 7: return launch_tile_finish_g<7>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 8: return launch_tile_finish_g<8>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int G>
 static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
                                 float *raw_out, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
@@ -610,14 +642,7 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    KernelTimer timer(TRIA_TIMER_NORMALISE, st);
-    float *zst = (float *)(ws + lay.zst_off);
-    tile_stats_kernel<G><<<streams, kScoreThreads, 0, st>>>(part, pivot, N, lay.tiles, zst, stats, err);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int chunks = (N + kZmaxKeys - 1) / kZmaxKeys;
-    zmax_tiles_kernel<G><<<(unsigned)((long long)streams * chunks), kScoreThreads, 0, st>>>(raw, zst, N, chunks, F);
-    return hipGetLastError();
+    return launch_tile_finish(G, streams, N, raw, part, pivot, F, stats, lay, ws, st);
 }
 
 hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,

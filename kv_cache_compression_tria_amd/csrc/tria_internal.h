@@ -70,6 +70,14 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
 int mfma_ops_per_stream(int G);   // 16-byte operand words per lane and stream (prologue output)
 hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
                              float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+// per-head statistics and z-max of the tiled paths over raw [streams][G][N] and the tile partials
+// part [streams][tiles][G][4] (sums around pivot[stream][h], or around 0 when pivot is null)
+hipError_t launch_tile_finish(int G, int streams, int N, const float *raw, const double *part, const float *pivot,
+                              float *F, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+// TRIA_PER_KEY_PHASE / TRIA_KEYS_PRE_ROPE scoring (vector ALU, any dtype)
+hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
+                               const int32_t *t, int n_seq, int N, unsigned flags, float *F, float *raw_out,
+                               float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
 hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
                        float *stats, hipStream_t st);
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st);

@@ -168,11 +168,12 @@ def draw_calibration(rng, cfg: Config, L: int | None = None):
             np.ascontiguousarray(R, dtype=np.float32))
 
 
-def make_host(cfg: Config, n_seq: int | None = None, n_layers: int | None = None):
+def make_host(cfg: Config, n_seq: int | None = None, n_layers: int | None = None, pre_rope: bool = False):
     """Draw a whole workload on the host with numpy.
 
     Returns a dict: k, v [S][L][Hkv][N][d] (float32 or uint16 bf16 bits), pos [S][L][Hkv][N]
     int32, t [S] int32, qc [L][Hq][d], qn, rb [L][Hq][d/2] float32, plus the config.
+    With ``pre_rope`` the cache holds the keys before RoPE (same draws, no rotation).
     """
     rng = np.random.Generator(np.random.PCG64(cfg.seed))
     S = cfg.n_seq if n_seq is None else n_seq
@@ -194,7 +195,7 @@ def make_host(cfg: Config, n_seq: int | None = None, n_layers: int | None = None
             for g in range(Hkv):
                 pos[s, l, g] = draw_positions(rng, N, int(t[s]), cfg.positions)
             pre = kc[l][:, None, :] + 0.5 * rng.standard_normal((Hkv, N, d))
-            post = rope_fp64(pre, pos[s, l], w).astype(np.float32)
+            post = (pre if pre_rope else rope_fp64(pre, pos[s, l], w)).astype(np.float32)
             vv = rng.standard_normal((Hkv, N, d)).astype(np.float32)
             if cfg.dtype == "f32":
                 k[s, l], v[s, l] = post, vv
@@ -203,11 +204,13 @@ def make_host(cfg: Config, n_seq: int | None = None, n_layers: int | None = None
     return {"cfg": cfg, "k": k, "v": v, "pos": pos, "t": t, "qc": qc, "qn": qn, "rb": rb}
 
 
-def make_device(cfg: Config, device="cuda", n_seq: int | None = None, n_layers: int | None = None):
+def make_device(cfg: Config, device="cuda", n_seq: int | None = None, n_layers: int | None = None,
+                pre_rope: bool = False):
     """Draw a workload directly in device memory with torch (large configurations).
 
     Same recipe and layout as ``make_host``; K and V are torch tensors of dtype float32 or
     bfloat16 on ``device``.  Calibration statistics are drawn on the host (they are small).
+    With ``pre_rope`` the cache holds the keys before RoPE.
     """
     import torch
 
@@ -242,13 +245,17 @@ def make_device(cfg: Config, device="cuda", n_seq: int | None = None, n_layers: 
         for l in range(L):
             pre = kc[l][:, None, :] + 0.5 * torch.randn((Hkv, N, d), generator=gen, device=device,
                                                          dtype=torch.float64)
-            a = p[l].to(torch.float64)[..., None] * w
-            c, sn = torch.cos(a), torch.sin(a)
-            xr, xi = pre[..., :h], pre[..., h:]
-            post = torch.cat([xr * c - xi * sn, xr * sn + xi * c], dim=-1)
+            if pre_rope:
+                post = pre
+            else:
+                a = p[l].to(torch.float64)[..., None] * w
+                c, sn = torch.cos(a), torch.sin(a)
+                xr, xi = pre[..., :h], pre[..., h:]
+                post = torch.cat([xr * c - xi * sn, xr * sn + xi * c], dim=-1)
+                del a, c, sn
             k[s, l] = post.to(torch.float32).to(tdt)
             v[s, l] = torch.randn((Hkv, N, d), generator=gen, device=device).to(tdt)
-            del pre, a, c, sn, post
+            del pre, post
     t_dev = torch.from_numpy(t).to(device)
     return {"cfg": cfg, "k": k, "v": v, "pos": pos, "t": t, "t_dev": t_dev, "qc": qc, "qn": qn, "rb": rb}
 

@@ -11,6 +11,8 @@ Tolerances (fp32 accumulation against fp64):
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 
 import synth
@@ -104,3 +106,39 @@ def streams_of(x, N):
 
 def host_cache(x):
     return synth.cache_to_host(x)
+
+
+def variant(base: int, **kw):
+    return dataclasses.replace(synth.CONFIGS[base], **kw)
+
+
+def run_case(orc, T, cfg, form="fac", sample=None, flags=0):
+    print(f"\n[case] {cfg.describe()} form={form} flags={flags}", flush=True)
+    pre_rope = bool(flags & T.KEYS_PRE_ROPE)
+    wl = synth.make_host(cfg, pre_rope=pre_rope)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    N, B = cfg.n_keys, cfg.budget
+    kb, vb, pb = streams_of(wl["k"], N), streams_of(wl["v"], N), streams_of(wl["pos"], N)
+    out = gpu_prune(T, calib, dev, B, flags=flags)
+    ids = np.arange(cfg.n_streams) if sample is None else np.asarray(sample)
+    res = orc.prune_streams(kb[ids], pb[ids], wl["t"], wl["qc"], wl["qn"], wl["rb"], B, cfg.n_kv_heads,
+                            stream_ids=ids, form=form, want_raw=True, pre_rope=pre_rope)
+    e_raw = check_raw(out["raw"][ids], res["raw"])
+    e_F = check_F(out["F"][ids], res["F"])
+    n_diff = check_kept_sets(out["kept"][ids], res["kept"], res["F"], B)
+    check_select_exact(orc, out["kept"][ids], out["F"][ids], B)
+    mu = res["raw"].mean(axis=2)
+    sd = res["raw"].std(axis=2)
+    np.testing.assert_allclose(out["stats"][ids, :, 0], mu, rtol=1e-5, atol=1e-5 * np.abs(sd).max())
+    np.testing.assert_allclose(out["stats"][ids, :, 1], sd, rtol=1e-4)
+    ka = streams_of(host_cache(dev["k"]), N)
+    va = streams_of(host_cache(dev["v"]), N)
+    pa = streams_of(dev["pos"].cpu().numpy(), N)
+    check_compaction(kb[ids], ka[ids], out["kept"][ids], B)
+    check_compaction(vb[ids], va[ids], out["kept"][ids], B)
+    check_compaction(pb[ids], pa[ids], out["kept"][ids], B)
+    print(f"[ok] raw err {e_raw:.2e}  F err {e_F:.2e}  streams with near-threshold set differences {n_diff}",
+          flush=True)
+    calib.free()
+    return out, res

@@ -4,8 +4,6 @@ Covers the small configurations in full, group sizes 1..8, both scoring paths (r
 on chip, and the tiled path with a ragged last tile), fp32 and bf16 caches, and the degenerate
 cases (one key, B >= N, constant streams, ties, non-finite keys).
 """
-import dataclasses
-
 import numpy as np
 import pytest
 
@@ -24,39 +22,8 @@ def T():
     return T
 
 
-def variant(base: int, **kw):
-    return dataclasses.replace(synth.CONFIGS[base], **kw)
-
-
-def run_case(orc, T, cfg, form="fac", sample=None, flags=0):
-    print(f"\n[case] {cfg.describe()} form={form} flags={flags}", flush=True)
-    wl = synth.make_host(cfg)
-    dev = synth.to_device(wl)
-    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
-    N, B = cfg.n_keys, cfg.budget
-    kb, vb, pb = gc.streams_of(wl["k"], N), gc.streams_of(wl["v"], N), gc.streams_of(wl["pos"], N)
-    out = gc.gpu_prune(T, calib, dev, B, flags=flags)
-    ids = np.arange(cfg.n_streams) if sample is None else np.asarray(sample)
-    res = orc.prune_streams(kb[ids], pb[ids], wl["t"], wl["qc"], wl["qn"], wl["rb"], B, cfg.n_kv_heads,
-                            stream_ids=ids, form=form, want_raw=True)
-    e_raw = gc.check_raw(out["raw"][ids], res["raw"])
-    e_F = gc.check_F(out["F"][ids], res["F"])
-    n_diff = gc.check_kept_sets(out["kept"][ids], res["kept"], res["F"], B)
-    gc.check_select_exact(orc, out["kept"][ids], out["F"][ids], B)
-    mu = res["raw"].mean(axis=2)
-    sd = res["raw"].std(axis=2)
-    np.testing.assert_allclose(out["stats"][ids, :, 0], mu, rtol=1e-5, atol=1e-5 * np.abs(sd).max())
-    np.testing.assert_allclose(out["stats"][ids, :, 1], sd, rtol=1e-4)
-    ka = gc.streams_of(gc.host_cache(dev["k"]), N)
-    va = gc.streams_of(gc.host_cache(dev["v"]), N)
-    pa = gc.streams_of(dev["pos"].cpu().numpy(), N)
-    gc.check_compaction(kb[ids], ka[ids], out["kept"][ids], B)
-    gc.check_compaction(vb[ids], va[ids], out["kept"][ids], B)
-    gc.check_compaction(pb[ids], pa[ids], out["kept"][ids], B)
-    print(f"[ok] raw err {e_raw:.2e}  F err {e_F:.2e}  streams with near-threshold set differences {n_diff}",
-          flush=True)
-    calib.free()
-    return out, res
+variant = gc.variant
+run_case = gc.run_case
 
 
 def test_config1_tiny_fp32_literal_oracle(orc, T):

@@ -1,0 +1,108 @@
+"""GPU parity of the scoring variants that need each key's position (run on an MI355X).
+
+TRIA_PER_KEY_PHASE scores post-RoPE keys in the literal per-key form (phase recovery of every
+band, then the distance phase w_f (t - p_j)); TRIA_KEYS_PRE_ROPE scores a cache that keeps keys
+before RoPE.  Both run through the C ABI and are compared with the fp64 oracle (its post-RoPE or
+pre-RoPE mode) to the same bars as the default path: raw and final scores within 1e-4 relative,
+kept sets equal up to near-threshold keys, selection and compaction bit-exact.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests import gpu_check as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_compression_tria_amd as T
+    T.lib()
+    return T
+
+
+def test_per_key_phase_config2_literal_oracle(orc, T):
+    gc.run_case(orc, T, synth.CONFIGS[2], form="lit", flags=T.PER_KEY_PHASE)
+
+
+def test_keys_pre_rope_config1_fp32_literal_oracle(orc, T):
+    gc.run_case(orc, T, synth.CONFIGS[1], form="lit", flags=T.KEYS_PRE_ROPE)
+
+
+def test_keys_pre_rope_config2(orc, T):
+    gc.run_case(orc, T, synth.CONFIGS[2], flags=T.KEYS_PRE_ROPE)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("flags", [1, 2])
+def test_variant_group_sizes(orc, T, G, flags):
+    cfg = gc.variant(2, name=f"var{flags}-g{G}", n_q_heads=2 * G, n_kv_heads=2, n_seq=2, n_keys=700, budget=500,
+                     t_fixed=9000, calib="uniform_r", r_range=(0.6, 0.99), seed=300 + G)
+    gc.run_case(orc, T, cfg, flags=flags)
+
+
+@pytest.mark.parametrize("G,dtype,N,flags", [(8, "bf16", 5000, 1), (8, "bf16", 5000, 2), (3, "f32", 7000, 1),
+                                             (3, "f32", 7000, 3)])
+def test_variant_ragged_tiles(orc, T, G, dtype, N, flags):
+    """Several 1024-key tiles with a ragged last one; flags 3 (both set) is the pre-RoPE form."""
+    cfg = gc.variant(2, name=f"var{flags}-g{G}-{dtype}-N{N}", n_q_heads=G, n_kv_heads=1, n_seq=3, n_keys=N,
+                     budget=N // 3 + 7, dtype=dtype, t_fixed=N + 1000, calib="head_r", r_range=(0.6, 0.99),
+                     seed=320 + G)
+    gc.run_case(orc, T, cfg, flags=flags)
+
+
+def test_per_key_phase_large_positions(orc, T):
+    """Positions up to 9e4: band 0 turns 14000 times; the exact range reduction keeps the phase."""
+    cfg = gc.variant(2, name="var1-long", n_q_heads=2, n_kv_heads=1, n_seq=1, n_keys=70001, budget=7000,
+                     t_fixed=90000, calib="head_r", r_range=(0.6, 0.99), seed=330)
+    gc.run_case(orc, T, cfg, flags=T.PER_KEY_PHASE)
+
+
+def test_per_key_phase_agrees_with_default_path(T):
+    """Same post-RoPE cache scored both ways: final scores agree to 2e-4 relative (both are within
+    1e-4 of the oracle), and the kept sets match except at near-ties."""
+    import torch
+    cfg = gc.variant(5, name="c5-shape-small", n_layers=2, n_seq=1, n_keys=4096, budget=384, t_fixed=4095)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    F0 = T.score(calib, dev["k"], dev["t_dev"], check=True)
+    F1 = T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=T.PER_KEY_PHASE, check=True)
+    torch.cuda.synchronize()
+    a, b = F0.cpu().numpy().astype(np.float64), F1.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(a - b) / np.maximum(np.abs(a), 1.0)) <= 2e-4
+    calib.free()
+
+
+def test_variant_budget_one_and_single_key(orc, T):
+    gc.run_case(orc, T, gc.variant(2, name="var-b1", n_q_heads=8, n_kv_heads=2, n_keys=300, budget=1, seed=341),
+                flags=T.KEYS_PRE_ROPE)
+    out, _ = gc.run_case(orc, T, gc.variant(2, name="var-bN", n_q_heads=8, n_kv_heads=2, n_keys=300, budget=300,
+                                            seed=342), flags=T.PER_KEY_PHASE)
+    assert np.array_equal(out["kept"], np.tile(np.arange(300), (2, 1)))
+    import torch
+    cfg = gc.variant(2, name="var-n1", n_q_heads=4, n_kv_heads=1, n_keys=1, budget=1, t_fixed=5000, seed=343,
+                     positions="contiguous")
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1)
+    for flags in (T.PER_KEY_PHASE, T.KEYS_PRE_ROPE):
+        F = T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=flags, check=True)
+        torch.cuda.synchronize()
+        assert F.cpu().numpy().ravel().tolist() == [0.0]
+    calib.free()
+
+
+def test_variant_requires_positions(T):
+    """The variants read key positions: a null pos is rejected before any launch."""
+    cfg = gc.variant(2, name="var-nopos", n_q_heads=4, n_kv_heads=1, n_keys=64, budget=8, seed=344,
+                     positions="contiguous")
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1)
+    with pytest.raises(T.TriaError):
+        T.score(calib, dev["k"], dev["t_dev"], flags=T.PER_KEY_PHASE)
+    calib.free()
