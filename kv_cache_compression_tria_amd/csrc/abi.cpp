@@ -91,6 +91,7 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     std::vector<double2> P(nh * TRIA_HALF);
     std::vector<float2> P32(nh * TRIA_HALF);
     std::vector<float> W(nh * TRIA_HALF);
+    std::vector<float> PW(nh * TRIA_HALF * 3);   // [L][Hkv][64][3][G]: Re P, Im P, W of the group
     for (size_t hh = 0; hh < nh; ++hh) {
         for (int f = 0; f < TRIA_HALF; ++f) {
             const double qr = qc[hh * TRIA_D + f], qi = qc[hh * TRIA_D + TRIA_HALF + f];
@@ -99,6 +100,11 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
             P[hh * TRIA_HALF + f] = make_double2(pr, pi);
             P32[hh * TRIA_HALF + f] = make_float2((float)pr, (float)pi);
             W[hh * TRIA_HALF + f] = (float)((1.0 - (double)rb[hh * TRIA_HALF + f]) * (double)qn[hh * TRIA_HALF + f]);
+            const size_t grp = hh / G, h = hh % G;
+            float *pw = &PW[((grp * TRIA_HALF + f) * 3) * G + h];
+            pw[0] = P32[hh * TRIA_HALF + f].x;
+            pw[G] = P32[hh * TRIA_HALF + f].y;
+            pw[2 * G] = W[hh * TRIA_HALF + f];
         }
     }
 
@@ -111,19 +117,22 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     const size_t bP32 = tria::align256(sizeof(float2) * P32.size());
     const size_t bW = tria::align256(sizeof(float) * W.size());
     const size_t bnu = tria::align256(sizeof(uint64_t) * TRIA_HALF);
-    c->block_bytes = bP + bP32 + bW + bnu;
+    const size_t bPW = tria::align256(sizeof(float) * PW.size());
+    c->block_bytes = bP + bP32 + bW + bnu + bPW;
     if (hipMalloc(&c->block, c->block_bytes) != hipSuccess) { delete c; return TRIA_E_NOMEM; }
     char *b = (char *)c->block;
     c->P = (double2 *)b;
     c->P32 = (float2 *)(b + bP);
     c->W = (float *)(b + bP + bP32);
     c->nu = (uint64_t *)(b + bP + bP32 + bW);
+    c->PW = (float *)(b + bP + bP32 + bW + bnu);
     hipStream_t st = (hipStream_t)stream;
     bool ok = hipStreamSynchronize(st) == hipSuccess;
     ok = ok && hipMemcpy(c->P, P.data(), sizeof(double2) * P.size(), hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->P32, P32.data(), sizeof(float2) * P32.size(), hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->W, W.data(), sizeof(float) * W.size(), hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->nu, nu.data(), sizeof(uint64_t) * TRIA_HALF, hipMemcpyHostToDevice) == hipSuccess;
+    ok = ok && hipMemcpy(c->PW, PW.data(), sizeof(float) * PW.size(), hipMemcpyHostToDevice) == hipSuccess;
     if (!ok) {
         (void)hipFree(c->block);
         delete c;

@@ -11,8 +11,9 @@
 // The norm score is sum_f W_f |k_f| with W_f = (1 - R_f) E|q_f| (|k_f| = |ktilde_f|).
 // Phases use the exact integer range reduction of the query rotation: w_f / 2pi is a 64-bit
 // fraction of a turn (nu_f), n * nu_f mod 2^64 is exact for any integer n, and its top 32 bits
-// give the angle in turns for sincospi.  Per band the key is turned by exp(-i w_f (t - p)) once,
-// then every head costs two FMAs: Re[P_f conj(k e^{-i phi})].
+// give the angle in turns for the hardware sine and cosine.  Per band the key is turned by
+// exp(-i w_f (t - p)) once, then every head costs three FMAs: Re[P_f conj(k e^{-i phi})] and
+// W_f |k_f|.  The group's constants are wave-uniform and come through the scalar cache.
 //
 // One block scores one 1024-key tile of one stream (one thread per key, four keys per thread) and
 // writes, like the matrix-core tile kernel, raw scores head-major [streams][G][N] and the tile's
@@ -32,8 +33,17 @@ __device__ __forceinline__ float turns_of(int64_t n, uint64_t nu)
     return (float)(int32_t)(uint32_t)(prod >> 32) * 0x1p-32f;
 }
 
+// sin and cos of 2 pi r for r in turns: the hardware sine / cosine take their argument in turns,
+// and |r| <= 1/2 lies well inside their accurate range
+__device__ __forceinline__ void sincos_turns(float r, float &s, float &c)
+{
+    s = __builtin_amdgcn_sinf(r);
+    c = __builtin_amdgcn_cosf(r);
+}
+
+// Eight bands of a key row: real parts of bands f0..f0+7 and the matching imaginary parts.
 template <bool BF16>
-__device__ __forceinline__ void load_band_group(const void *__restrict__ row, int f0, float (&re)[8], float (&im)[8])
+__device__ __forceinline__ void load_band_group(const char *__restrict__ row, int f0, float (&re)[8], float (&im)[8])
 {
     if (BF16) {
         const uint4 *r = (const uint4 *)row;                 // 128 bf16 = 16 x 16 B
@@ -67,29 +77,18 @@ struct KSums {
 template <int G, bool BF16, bool PRE_ROPE>
 __global__ __launch_bounds__(kScoreThreads) void score_perkey_tile_kernel(
     const void *__restrict__ k, const int32_t *__restrict__ pos, const int32_t *__restrict__ t,
-    const float2 *__restrict__ P32, const float *__restrict__ W, const uint64_t *__restrict__ nu, int L, int Hkv,
-    int N, int tiles, float *__restrict__ raw, double *__restrict__ part)
+    const float *__restrict__ PW, const uint64_t *__restrict__ nu, int L, int Hkv, int N, int tiles,
+    float *__restrict__ raw, double *__restrict__ part)
 {
     constexpr int RW = BF16 ? 256 : 512;     // row bytes
-    __shared__ float2 sP[G][TRIA_HALF];
-    __shared__ float sW[G][TRIA_HALF];
-    __shared__ uint64_t sNu[TRIA_HALF];
     __shared__ KSums red[kScoreThreads / 64][G];
 
     const int sid = blockIdx.x / tiles;
     const int tile = blockIdx.x - sid * tiles;
-    const int g = sid % Hkv;
-    const int l = (sid / Hkv) % L;
     const int s = sid / (Hkv * L);
-    const int Hq = Hkv * G;
-    for (int i = threadIdx.x; i < G * TRIA_HALF; i += kScoreThreads) {
-        const int h = i / TRIA_HALF, f = i - h * TRIA_HALF;
-        const size_t hh = (size_t)l * Hq + g * G + h;
-        sP[h][f] = P32[hh * TRIA_HALF + f];
-        sW[h][f] = W[hh * TRIA_HALF + f];
-    }
-    for (int f = threadIdx.x; f < TRIA_HALF; f += kScoreThreads) sNu[f] = nu[f];
-    __syncthreads();
+    // the group's constants, band-major: Re P (G), Im P (G), W (G) per band.  Every lane reads the
+    // same words, so they arrive through the scalar cache into scalar registers.
+    const float *pw = PW + (size_t)(sid % (Hkv * L)) * TRIA_HALF * 3 * G;
 
     const int64_t ts = t[s];
     const int j0 = tile * kTileKeys;
@@ -115,22 +114,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_perkey_tile_kernel(
                 if (!PRE_ROPE) {
                     // recover the pre-RoPE band: k = ktilde * exp(-i w_f p)
                     float sp, cp;
-                    sincospif(2.f * turns_of(p, sNu[f]), &sp, &cp);
+                    sincos_turns(turns_of(p, nu[f]), sp, cp);
                     const float r2 = kr * cp + ki * sp, i2 = ki * cp - kr * sp;
                     kr = r2;
                     ki = i2;
                 }
-                const float mag = sqrtf(kr * kr + ki * ki);
+                const float mag = __builtin_amdgcn_sqrtf(fmaf(kr, kr, ki * ki));
                 // distance phase w_f (t - p): turn the key by exp(-i phi)
                 float sd, cd;
-                sincospif(2.f * turns_of(ts - p, sNu[f]), &sd, &cd);
+                sincos_turns(turns_of(ts - p, nu[f]), sd, cd);
                 const float ur = kr * cd + ki * sd, ui = ki * cd - kr * sd;
+                const float *c = pw + f * 3 * G;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const float2 P = sP[h][f];
-                    acc[h] = fmaf(P.x, ur, acc[h]);
-                    acc[h] = fmaf(P.y, ui, acc[h]);
-                    acc[h] = fmaf(sW[h][f], mag, acc[h]);
+                    acc[h] = fmaf(c[h], ur, acc[h]);
+                    acc[h] = fmaf(c[G + h], ui, acc[h]);
+                    acc[h] = fmaf(c[2 * G + h], mag, acc[h]);
                 }
             }
         }
@@ -186,7 +185,7 @@ static hipError_t launch_perkey_t(const tria_calib *c, const void *k, const int3
     const long long blocks = (long long)streams * tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     score_perkey_tile_kernel<G, BF16, PRE_ROPE><<<(unsigned)blocks, kScoreThreads, 0, st>>>(
-        k, pos, t, c->P32, c->W, c->nu, c->L, c->Hkv, N, tiles, raw, part);
+        k, pos, t, c->PW, c->nu, c->L, c->Hkv, N, tiles, raw, part);
     return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct tria_calib {
     float2 *P32;     // [L][Hq][64] the same rounded to fp32
     float *W;        // [L][Hq][64] norm weights (1 - R_f) E|q_f|
     uint64_t *nu;    // [64] w_f / (2 pi) as a 64-bit fraction of a turn
+    float *PW;       // [L][Hkv][64][3][G] Re P32, Im P32 and W of each KV group, band-major
 };
 
 // Workspace layout of tria_score (every region 256-byte aligned).
