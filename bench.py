@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--score-path", choices=("auto", "tiled"), default="auto",
+                    help="long-stream bf16 scoring: auto (stream clusters keep raw scores on chip) or tiled")
     ap.add_argument("--variant", choices=VARIANTS, default="default",
                     help="scoring form: default (post-RoPE keys, rotated queries), per_key_phase (post-RoPE "
                          "keys, literal per-key phases), pre_rope (keys cached before RoPE)")
@@ -104,6 +106,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     T.lib()   # fail loudly if the HIP library is missing
+    T.set_score_path(T.PATH_TILED if args.score_path == "tiled" else T.PATH_AUTO)
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -211,7 +214,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "streams": n_streams, "keys_per_stream": N, "budget": B,
                    "layers": L, "seqs": S, "q_heads": cfg.n_q_heads, "kv_heads": Hkv, "head_dim": d,
-                   "cache_dtype": cfg.dtype, "score_variant": args.variant, "parallelism": "single-gpu"},
+                   "cache_dtype": cfg.dtype, "score_variant": args.variant, "score_path": args.score_path, "parallelism": "single-gpu"},
         "alg_bytes_per_step": int(alg),
         "alg_GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

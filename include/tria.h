@@ -114,7 +114,8 @@ tria_status tria_score(const tria_calib *calib, tria_dtype dtype, const void *k,
                        float *head_stats, unsigned flags, void *ws, size_t ws_bytes, void *stream);
 
 /* Synchronise `stream` and report TRIA_E_NONFINITE if the last tria_score on this workspace
- * met a non-finite score, else TRIA_OK (TRIA_E_DEVICE on a runtime error). */
+ * met a non-finite score, else TRIA_OK (TRIA_E_DEVICE on a runtime error, or when a stream
+ * cluster's exchange of partial sums did not complete). */
 tria_status tria_score_check(const void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes tria_select_topB needs (0 on bad arguments). */
@@ -166,6 +167,19 @@ typedef enum {
 
 tria_status tria_timing_enable(int on);
 tria_status tria_timing_read(double *ms /* [TRIA_TIMER_COUNT] */, int *launches /* [TRIA_TIMER_COUNT] */);
+
+/*
+ * Scoring path for bf16 streams too long for one block's LDS (process-wide; for tests and
+ * measurement).  TRIA_PATH_AUTO (default): a cooperative grid of one block per CU in which the
+ * blocks of a stream cluster keep its raw scores in LDS and exchange per-head partial sums, when
+ * the device supports cooperative launch and the stream fits 32 blocks; else the tiled path.
+ * TRIA_PATH_TILED: always the tiled path (raw scores through the workspace, separate statistics
+ * and z-max kernels).  Both give the same scores within rounding.  Errors: INVALID (unknown path).
+ * The cluster path reports a cluster exchange that never completed as TRIA_E_DEVICE from
+ * tria_score_check.
+ */
+typedef enum { TRIA_PATH_AUTO = 0, TRIA_PATH_TILED = 1 } tria_score_path;
+tria_status tria_set_score_path(int path);
 
 #ifdef __cplusplus
 }

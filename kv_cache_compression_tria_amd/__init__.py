@@ -27,6 +27,7 @@ EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
+    "tria_set_score_path",
 )
 TIMERS = ("score_keys", "normalise", "select", "compact")
 
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.tria_status_string.argtypes = [I]
         L.tria_timing_enable.restype = I
         L.tria_timing_enable.argtypes = [I]
+        L.tria_set_score_path.restype = I
+        L.tria_set_score_path.argtypes = [I]
         L.tria_timing_read.restype = I
         L.tria_timing_read.argtypes = [ctypes.POINTER(D), ctypes.POINTER(I)]
         _lib = L
@@ -263,6 +266,15 @@ def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int
                           _stream(stream))
     _check(st, "tria_prune")
     return F, kept
+
+
+PATH_AUTO = 0
+PATH_TILED = 1
+
+
+def set_score_path(path: int):
+    """Choose the long-stream bf16 scoring path (``tria_set_score_path``): PATH_AUTO or PATH_TILED."""
+    _check(lib().tria_set_score_path(int(path)), "tria_set_score_path")
 
 
 def timing_enable(on: bool = True):

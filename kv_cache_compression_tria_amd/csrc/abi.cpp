@@ -27,6 +27,10 @@ uint64_t turn_fraction(double w)
 
 }  // namespace
 
+namespace tria {
+std::atomic<int> g_score_path{TRIA_PATH_AUTO};
+}
+
 extern "C" {
 
 const char *tria_status_string(tria_status s)
@@ -205,7 +209,15 @@ tria_status tria_score_check(const void *ws, size_t ws_bytes, void *stream)
     hipStream_t st = (hipStream_t)stream;
     if (hipMemcpyAsync(&flag, ws, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return TRIA_E_DEVICE;
     if (hipStreamSynchronize(st) != hipSuccess) return TRIA_E_DEVICE;
+    if (flag & 2) return TRIA_E_DEVICE;
     return flag ? TRIA_E_NONFINITE : TRIA_OK;
+}
+
+tria_status tria_set_score_path(int path)
+{
+    if (path != TRIA_PATH_AUTO && path != TRIA_PATH_TILED) return TRIA_E_INVALID;
+    tria::g_score_path.store(path);
+    return TRIA_OK;
 }
 
 size_t tria_select_workspace_bytes(int n_streams, int n_keys, int budget)

@@ -42,6 +42,12 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
         off += align256(streams * (size_t)mfma_ops_per_stream(c->G) * 64 * 16);
         w.pivot_off = off;
         off += align256(heads * sizeof(float));
+        // partial sums exchanged inside stream clusters (two round slots per block) and the
+        // clusters' arrival counters
+        w.xpart_off = off;
+        off += align256((size_t)kClusterMaxBlocks * 2 * TRIA_MAX_G * 4 * sizeof(double));
+        w.arrive_off = off;
+        off += align256((size_t)kClusterMaxBlocks * sizeof(uint32_t));
     }
     {
         // raw scores, tile partials and per-head mean / 1/std: used by the tiled paths and by the

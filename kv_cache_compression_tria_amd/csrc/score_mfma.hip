@@ -141,12 +141,15 @@ __device__ __forceinline__ void load_tile(u32x4 (&ka)[4], const u32x4 *__restric
 }
 
 // v_permlane32_swap: lanes 32..63 of x trade places with lanes 0..31 of y, so that afterwards
-// x = (x[0..31], y[0..31]) and y = (x[32..63], y[32..63]).  Written as inline asm because the
-// compiler's builtin for it drops its second result; the s_nop pairs cover the wait states
-// around a cross-lane VALU operation.
+// x = (x[0..31], y[0..31]) and y = (x[32..63], y[32..63]).  Through the compiler builtin, so that
+// the wait states after the matrix-core instruction that produced x and y (its result is not
+// interlocked for this read) are inserted by the compiler's hazard recognizer.
 __device__ __forceinline__ void permlane32_swap(float &x, float &y)
 {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y),
+                                                    false, false);
+    x = __builtin_bit_cast(float, (uint32_t)r[0]);
+    y = __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 // re^2 + im^2 of a band held as a bf16 pair (re, im) in fp32 (v_dot2: products exact, one
@@ -256,13 +259,16 @@ __device__ __forceinline__ void finish_moments(const Sums &m, double p, double n
 }
 
 // Per-block reduction of the lane sums: waves publish their 16-lane row sums to LDS, thread h
-// (< G) adds the 4 waves in order.
-struct BlockSums {
-    double s1[4][8], s2[4][8];
-    float mn[4][8], mx[4][8];
+// (< G) adds the NW waves in order.
+template <int NW>
+struct BlockSumsT {
+    double s1[NW][8], s2[NW][8];
+    float mn[NW][8], mx[NW][8];
 };
+using BlockSums = BlockSumsT<4>;
 
-__device__ __forceinline__ void block_sums_stage(BlockSums &bs, Sums (&m)[2])
+template <int NW>
+__device__ __forceinline__ void block_sums_stage(BlockSumsT<NW> &bs, Sums (&m)[2])
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int j = lane & 15, g = lane >> 4;
@@ -279,12 +285,13 @@ __device__ __forceinline__ void block_sums_stage(BlockSums &bs, Sums (&m)[2])
     }
 }
 
-__device__ __forceinline__ Sums block_sums_of(const BlockSums &bs, int h)
+template <int NW>
+__device__ __forceinline__ Sums block_sums_of(const BlockSumsT<NW> &bs, int h)
 {
     Sums t;
     t.init();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
         Sums u;
         u.s1 = bs.s1[w][h]; u.s2 = bs.s2[w][h]; u.mn = bs.mn[w][h]; u.mx = bs.mx[w][h];
         t.add(u);
@@ -573,6 +580,246 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_fused_kernel(
     }
 }
 
+// ---- cluster path: the raw scores of a stream stay on chip ----------------------------------
+// A stream too long for one block's LDS is split over a cluster of Ps blocks (Ps a power of two),
+// each keeping the raw scores of its Kb keys in LDS ([Kb][GP] floats, key-major, GP = G rounded up
+// to even).  After scoring, every block publishes its per-head partial sums, waits until the
+// cluster's Ps partials of this round are there, adds them in part order (every block gets the
+// same bits), and writes the final scores of its keys straight from LDS: the raw scores never
+// travel through HBM.  The grid is one block per CU, launched cooperatively so that all blocks
+// are resident at once; a block loops over rounds, cluster c scoring streams c, c + C, c + 2C, ...
+// The Ps blocks of a cluster sit on one XCD (workgroups are dealt to the 8 XCDs in turn), so
+// their exchange stays within that XCD's L2 in practice; correctness rests only on agent-scope
+// release / acquire.  Partial sums are double-buffered by round parity: a block can be at most
+// one round ahead of the slowest block of its cluster.  The wait is bounded: past the bound the
+// block sets bit 2 of the error flag and carries on (wrong scores, but no hang).
+constexpr int kClusterWaves = 8;
+constexpr unsigned kSpinLimit = 1u << 20;   // polls of about a microsecond each
+
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
+    int streams, int Ps, int Kb, int cpx, int C, double *__restrict__ xpart, uint32_t *__restrict__ arrive,
+    float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats, int *__restrict__ err)
+{
+    constexpr int GP = (G + 1) & ~1;
+    extern __shared__ float lraw[];                // [Kb][GP]
+    __shared__ BlockSumsT<NW> bs;
+    __shared__ float zmu[8], zinv[8];
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    const int cl = x * cpx + y / Ps, part = y % Ps;
+    const int rounds = cl < streams ? (streams - cl + C - 1) / C : 0;
+    if (rounds == 0) return;                       // the whole cluster has no stream
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jj = lane & 15, ha = head_a(lane >> 4);
+    const int j0 = part * Kb;
+    const int nkeys = max(0, min(Kb, N - j0));
+    const int ntiles16 = (nkeys + 15) >> 4;
+    // Every wave takes the same number of items per round, a multiple of four (empty items re-read
+    // a real tile and score nothing), so that the four-deep ring runs on across rounds: the loads
+    // of the next round's first tiles are in flight while a round ends (exchange, statistics,
+    // final scores).
+    const int nt = (max(1, (ntiles16 + NW - 1) / NW) + 3) & ~3;
+    const int total = rounds * nt;
+
+    WaveScorer<G> ws;
+    ws.begin(ops, pivot, cl);
+    auto issue = [&](u32x4 (&b)[4], int i) {
+        const int ic = min(i, total - 1);
+        const int r = ic / nt;
+        const int sid = cl + r * C;
+        const int t = min(wid + NW * (ic - r * nt), ntiles16 - 1);
+        if (t >= 0)
+            load_tile(b, k + ((size_t)sid * N + j0 + t * 16) * 16, nkeys - t * 16);
+        else
+            load_tile(b, k + (size_t)sid * N * 16, 0);   // a part with no keys: row 0, scored as empty
+    };
+    auto compute = [&](const u32x4 (&b)[4], int li) {
+        const int t = wid + NW * li;
+        float v[2];
+        ws.score(b, nkeys - t * 16, v);
+        const int key = t * 16 + jj;
+        if (key < nkeys) {
+            if (ha < GP) lraw[key * GP + ha] = v[0];
+            if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
+        }
+    };
+    u32x4 b0[4], b1[4], b2[4], b3[4];
+    issue(b0, 0);
+    TRIA_PIN();
+    issue(b1, 1);
+    TRIA_PIN();
+    issue(b2, 2);
+    TRIA_PIN();
+    for (int r = 0; r < rounds; ++r) {
+        for (int li = 0; li < nt; li += 4) {
+            const int i = r * nt + li;
+            issue(b3, i + 3);
+            TRIA_PIN();
+            compute(b0, li);
+            issue(b0, i + 4);
+            TRIA_PIN();
+            compute(b1, li + 1);
+            issue(b1, i + 5);
+            TRIA_PIN();
+            compute(b2, li + 2);
+            issue(b2, i + 6);
+            TRIA_PIN();
+            compute(b3, li + 3);
+            TRIA_PIN();
+        }
+
+        // ---- end of round r: exchange partial sums within the cluster, then final scores
+        const int sid = cl + r * C;
+        block_sums_stage(bs, ws.m);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            // The exchanged words are agent-scope atomics (coherent across the device without
+            // cache maintenance): the partials are stored, the stores are waited for, and only
+            // then is the arrival counted; a reader that sees the count reads them afterwards.
+            double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
+            for (int h = 0; h < G; ++h) {
+                const Sums t2 = block_sums_of(bs, h);
+                double *q = xr + ((size_t)part * G + h) * 4;
+                __hip_atomic_store(q + 0, t2.s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(q + 1, t2.s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(q + 2, (double)t2.mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(q + 3, (double)t2.mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __hip_atomic_fetch_add(&arrive[cl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t target = (uint32_t)(r + 1) * (uint32_t)Ps;
+            unsigned spins = 0;
+            while (__hip_atomic_load(&arrive[cl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                // give up past the bound, or at once when another block already gave up
+                if (++spins > kSpinLimit ||
+                    (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2)) {
+                    atomicOr(err, 2);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            asm volatile("" ::: "memory");
+            for (int h = 0; h < G; ++h) {
+                Sums t2;
+                t2.init();
+                for (int pp = 0; pp < Ps; ++pp) {
+                    double *q = xr + ((size_t)pp * G + h) * 4;
+                    Sums u;
+                    u.s1 = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    u.s2 = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    u.mn = (float)__hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    u.mx = (float)__hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    t2.add(u);
+                }
+                double mean, sd;
+                finish_moments(t2, (double)pivot[(size_t)sid * G + h], (double)N, mean, sd);
+                zmu[h] = (float)mean;
+                zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
+                if (part == 0) {
+                    if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
+                    if (stats) {
+                        stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
+                        stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        float *fo = F + (size_t)sid * N + j0;
+        for (int j = threadIdx.x; j < nkeys; j += NW * 64) {
+            float z = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[j * GP + h] - zmu[h]) * zinv[h]);
+            fo[j] = z;
+        }
+        if (raw_out)
+            for (int q = threadIdx.x; q < G * nkeys; q += NW * 64) {
+                const int h = q / nkeys, j = q - h * nkeys;
+                raw_out[((size_t)sid * G + h) * N + j0 + j] = lraw[j * GP + h];
+            }
+        if (r + 1 < rounds) ws.begin(ops, pivot, sid + C);
+        __syncthreads();                           // LDS raw, sums and zmu are reused next round
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t *__restrict__ p, int n, uint32_t v)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Cluster geometry for a stream of N keys, or false when the cluster path does not apply.
+struct ClusterPlan {
+    int Ps, Kb, nb, cpx, C;
+};
+
+static bool cluster_plan(int G, int N, ClusterPlan &pl)
+{
+    int dev = 0, n_cu = 0, coop = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
+        return false;
+    if (!coop || n_cu <= 0) return false;
+    const int GP = (G + 1) & ~1;
+    const int kmax = (kClusterLds / (GP * 4)) & ~15;
+    int Ps = 1;
+    while ((long long)Ps * kmax < N) Ps *= 2;
+    if (Ps > 32) return false;
+    pl.Ps = Ps;
+    pl.Kb = ((N + Ps - 1) / Ps + 15) & ~15;
+    pl.nb = (n_cu / (8 * Ps)) * 8 * Ps;
+    if (pl.nb <= 0 || pl.nb > kClusterMaxBlocks) return false;
+    pl.cpx = pl.nb / 8 / Ps;
+    pl.C = pl.nb / Ps;
+    return true;
+}
+
+template <int G>
+static hipError_t launch_cluster_g(const ClusterPlan &pl, const u32x4 *kp, const u32x4 *ops, const float *pivot,
+                                   int N, int streams, float *F, float *raw_out, float *stats,
+                                   const tria_score_ws &lay, char *ws, hipStream_t st)
+{
+    constexpr int NW = kClusterWaves;
+    constexpr int GP = (G + 1) & ~1;
+    const size_t lds = (size_t)pl.Kb * GP * 4;
+    hipError_t e;
+    uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);
+    fill_u32_kernel<<<(pl.C + 255) / 256, 256, 0, st>>>(arrive, pl.C, 0u);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    double *xpart = (double *)(ws + lay.xpart_off);
+    int *err = (int *)(ws + lay.err_off);
+    int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
+    void *args[] = {(void *)&kp, (void *)&ops, (void *)&pivot, &n, &S, &Ps, &Kb, &cpx, &C,
+                    (void *)&xpart, (void *)&arrive, (void *)&F, (void *)&raw_out, (void *)&stats, (void *)&err};
+    KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
+    return hipLaunchCooperativeKernel((const void *)score_mfma_cluster_kernel<G, NW>, dim3(pl.nb), dim3(NW * 64),
+                                      args, (unsigned)lds, st);
+}
+
+// Whether one block of the cluster kernel fits on every CU at once (cooperative launch needs it).
+template <int G>
+static bool cluster_fits(const ClusterPlan &pl)
+{
+    constexpr int NW = kClusterWaves;
+    constexpr int GP = (G + 1) & ~1;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)score_mfma_cluster_kernel<G, NW>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kClusterLds) != hipSuccess)
+            return false;
+        attr_set = true;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_cluster_kernel<G, NW>,
+                                                     NW * 64, (size_t)pl.Kb * GP * 4) != hipSuccess)
+        return false;
+    return per_cu >= 1;
+}
+
 // ---- launch ------------------------------------------------------------------------------------
 template <int G>
 static hipError_t launch_tile_finish_g(int streams, int N, const float *raw, const double *part, const float *pivot,
@@ -631,6 +878,9 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
         score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
+    ClusterPlan pl;
+    if (cluster_enabled() && cluster_plan(G, N, pl) && cluster_fits<G>(pl))
+        return launch_cluster_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
     // raw scores go straight into the caller's raw output when there is one (same layout)
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/tria.h"
 
 #define TRIA_D 128      // head_dim
@@ -28,7 +30,7 @@ struct tria_calib {
 
 // Workspace layout of tria_score (every region 256-byte aligned).
 struct tria_score_ws {
-    size_t qrot_off, raw_off, part_off, zst_off, err_off, ops_off, pivot_off, total;
+    size_t qrot_off, raw_off, part_off, zst_off, err_off, ops_off, pivot_off, xpart_off, arrive_off, total;
     int tiled;       // 1: the stream does not fit one block's LDS
     int tiles;       // key tiles (blocks) per stream on the tiled path
 };
@@ -38,6 +40,8 @@ namespace tria {
 constexpr int kTileKeys = 1024;       // keys per block on the tiled scoring path
 constexpr int kScoreThreads = 256;
 constexpr int kFusedLdsMax = 80 * 1024;   // raw scores of a stream kept on chip up to this size
+constexpr int kClusterLds = 128 * 1024;   // raw scores one block of a stream cluster keeps on chip
+constexpr int kClusterMaxBlocks = 1024;   // largest cluster grid the workspace has room for
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectLdsKeys = 34560;     // streams up to this many keys are selected from LDS (with 24 KB of
                                           // static LDS: within the 160 KB of a CU)
@@ -45,6 +49,9 @@ constexpr int kCompactThreads = 256;
 constexpr int kCompactRows = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+extern std::atomic<int> g_score_path;   // tria_score_path chosen by tria_set_score_path
+inline bool cluster_enabled() { return g_score_path.load() == TRIA_PATH_AUTO; }
 
 // Brackets the kernel launches of its scope with a HIP event pair on `st` when timing is enabled
 // (tria_timing_enable); does nothing otherwise.

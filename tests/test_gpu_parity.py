@@ -41,19 +41,66 @@ def test_group_sizes(orc, T, G):
     run_case(orc, T, cfg)
 
 
+@pytest.fixture(params=["auto", "tiled"])
+def path(request, T):
+    """Long bf16 streams: the stream-cluster path (auto) and the tiled path."""
+    T.set_score_path(T.PATH_TILED if request.param == "tiled" else T.PATH_AUTO)
+    yield request.param
+    T.set_score_path(T.PATH_AUTO)
+
+
 @pytest.mark.parametrize("G,dtype,N", [(8, "bf16", 5000), (4, "bf16", 5000), (3, "f32", 7000), (1, "bf16", 21000)])
-def test_tiled_path_ragged_tail(orc, T, G, dtype, N):
-    cfg = variant(2, name=f"tiled-g{G}-{dtype}-N{N}", n_q_heads=G, n_kv_heads=1, n_seq=3, n_keys=N,
+def test_tiled_path_ragged_tail(orc, T, path, G, dtype, N):
+    cfg = variant(2, name=f"tiled-g{G}-{dtype}-N{N}-{path}", n_q_heads=G, n_kv_heads=1, n_seq=3, n_keys=N,
                   budget=N // 3 + 7, dtype=dtype, t_fixed=N + 1000, calib="head_r", r_range=(0.6, 0.99),
                   seed=200 + G)
     run_case(orc, T, cfg)
 
 
-def test_tiled_path_long_stream(orc, T):
-    """A stream of 70001 keys: 69 tiles of 1024 keys, the last one ragged (369 keys)."""
-    cfg = variant(2, name="tiled-long", n_q_heads=2, n_kv_heads=1, n_seq=1, n_keys=70001, budget=7000,
+def test_tiled_path_long_stream(orc, T, path):
+    """A stream of 70001 keys: 69 tiles of 1024 keys, the last one ragged (369 keys); on the
+    cluster path 8 blocks of 8752 keys, the last one with 8737."""
+    cfg = variant(2, name=f"tiled-long-{path}", n_q_heads=2, n_kv_heads=1, n_seq=1, n_keys=70001, budget=7000,
                   t_fixed=90000, calib="head_r", r_range=(0.6, 0.99), seed=210)
     run_case(orc, T, cfg)
+
+
+def test_cluster_path_many_rounds(orc, T, path):
+    """160 streams of 5000 keys with G = 8: 2-block clusters, 128 of them per grid, so most
+    blocks run two rounds; sampled streams on both sides of the round boundary."""
+    cfg = variant(2, name=f"rounds-{path}", n_q_heads=64, n_kv_heads=8, n_seq=1, n_layers=20, n_keys=5000,
+                  budget=1500, t_fixed=6000, calib="head_r", r_range=(0.6, 0.99), seed=212)
+    run_case(orc, T, cfg, sample=np.array([0, 1, 77, 127, 128, 129, 150, 159]))
+
+
+def test_stream_beyond_cluster_reach(orc, T):
+    """G = 8 and 140000 keys need more than 32 blocks of on-chip raw scores: the tiled path
+    takes over by itself."""
+    cfg = variant(2, name="g8-N140000", n_q_heads=8, n_kv_heads=1, n_seq=1, n_keys=140000, budget=9000,
+                  t_fixed=150000, calib="head_r", r_range=(0.6, 0.99), seed=213)
+    run_case(orc, T, cfg)
+
+
+def test_cluster_and_tiled_paths_agree(T):
+    """Same cache scored on both long-stream paths: final scores within 2e-6 relative (both
+    are fp32 scores of the same matrix-core products; only the summation order of the
+    statistics differs)."""
+    import torch
+    cfg = variant(5, name="c5-shape-2layer", n_layers=2, n_seq=1, n_keys=32768, budget=3072, t_fixed=32767)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    try:
+        T.set_score_path(T.PATH_TILED)
+        F0 = T.score(calib, dev["k"], dev["t_dev"], check=True)
+        T.set_score_path(T.PATH_AUTO)
+        F1 = T.score(calib, dev["k"], dev["t_dev"], check=True)
+    finally:
+        T.set_score_path(T.PATH_AUTO)
+    torch.cuda.synchronize()
+    a, b = F0.cpu().numpy().astype(np.float64), F1.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(a - b) / np.maximum(np.abs(a), 1.0)) <= 2e-6
+    calib.free()
 
 
 def test_tiled_path_many_streams_ragged_tail(orc, T):
