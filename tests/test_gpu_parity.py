@@ -59,18 +59,19 @@ def test_tiled_path_ragged_tail(orc, T, path, G, dtype, N):
 
 def test_tiled_path_long_stream(orc, T, path):
     """A stream of 70001 keys: 69 tiles of 1024 keys, the last one ragged (369 keys); on the
-    cluster path 8 blocks of 8752 keys, the last one with 8737."""
+    cluster path (G = 2) 8 blocks of 8752 keys, the last one with 8737."""
     cfg = variant(2, name=f"tiled-long-{path}", n_q_heads=2, n_kv_heads=1, n_seq=1, n_keys=70001, budget=7000,
                   t_fixed=90000, calib="head_r", r_range=(0.6, 0.99), seed=210)
     run_case(orc, T, cfg)
 
 
 def test_cluster_path_many_rounds(orc, T, path):
-    """160 streams of 5000 keys with G = 8: 2-block clusters, 128 of them per grid, so most
-    blocks run two rounds; sampled streams on both sides of the round boundary."""
-    cfg = variant(2, name=f"rounds-{path}", n_q_heads=64, n_kv_heads=8, n_seq=1, n_layers=20, n_keys=5000,
-                  budget=1500, t_fixed=6000, calib="head_r", r_range=(0.6, 0.99), seed=212)
-    run_case(orc, T, cfg, sample=np.array([0, 1, 77, 127, 128, 129, 150, 159]))
+    """480 streams of 3000 keys with G = 8: one block per stream (128 KB of raw scores fit), 256
+    clusters per grid, so part of the grid runs a second round; sampled streams on both sides
+    of the round boundary."""
+    cfg = variant(2, name=f"rounds-{path}", n_q_heads=64, n_kv_heads=8, n_seq=1, n_layers=60, n_keys=3000,
+                  budget=900, t_fixed=4000, calib="head_r", r_range=(0.6, 0.99), seed=212)
+    run_case(orc, T, cfg, sample=np.array([0, 1, 200, 255, 256, 257, 479]))
 
 
 def test_stream_beyond_cluster_reach(orc, T):
