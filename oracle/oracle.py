@@ -54,6 +54,8 @@ def lib():
         L.oracle_prune_streams.restype = I
         L.oracle_prune_streams.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, D, P, I, I,
                                            P, I, P, P, P, I]
+        L.oracle_calib_stats.restype = None
+        L.oracle_calib_stats.argtypes = [I, I, I, I, P, P, P, P]
         L.oracle_max_threads.restype = I
         L.oracle_max_threads.argtypes = [I]
         _lib = L
@@ -179,6 +181,20 @@ def prune_streams(keys, pos, t, qc, qn, rb, B, n_kv_heads, stream_ids=None, thet
     if want_raw:
         out["raw"] = raw
     return out
+
+
+def calib_stats(q):
+    """Calibration statistics of captured pre-RoPE queries q [..., n_cal, d] (uint16 bf16 bits or
+    float32): returns (qbar [..., d], E|q_f| [..., d/2], R_f [..., d/2]) in float64."""
+    q = np.ascontiguousarray(q)
+    d, n_cal = q.shape[-1], q.shape[-2]
+    lead = q.shape[:-2]
+    n_heads = int(np.prod(lead)) if lead else 1
+    qc = np.zeros(lead + (d,))
+    qn = np.zeros(lead + (d // 2,))
+    r = np.zeros(lead + (d // 2,))
+    lib().oracle_calib_stats(n_heads, n_cal, d, _keys_dtype(q), _ptr(q), _ptr(qc), _ptr(qn), _ptr(r))
+    return qc, qn, r
 
 
 def max_threads(n_threads: int = 0) -> int:

@@ -291,6 +291,42 @@ int oracle_prune_streams(int form, int pre_rope, int dtype, int S, int L, int Hk
     return bad ? -1 : 0;
 }
 
+/*
+ * Calibration statistics of the captured pre-RoPE queries of every (layer, query head)
+ * (chenxutan.com/d/2624 section 3.4: centre vector, mean norm and concentration per head;
+ * zhichai.net section "破局之道": R as the ratio of the norm of the mean to the mean norm;
+ * watermelonwater.tech "TriAttention 方案设计" item 1: the Q centre and the expected norm).
+ * Per band f (the complex number q[f] + i q[f + d/2]):
+ *   qbar_f = mean_n q_{n,f}             (written back in the half-split layout)
+ *   E|q_f| = mean_n |q_{n,f}|
+ *   R_f    = |qbar_f| / E|q_f|          (0 when E|q_f| = 0)
+ *   q      : [n_heads][n_cal][d] (dtype 0 bf16 bits / 1 fp32), n_heads = L * Hq
+ *   qc_out : [n_heads][d];  qn_out, r_out : [n_heads][d/2]   (fp64)
+ */
+void oracle_calib_stats(int n_heads, int n_cal, int d, int dtype, const void *q, double *qc_out,
+                        double *qn_out, double *r_out)
+{
+    const int half = d / 2;
+    for (int hh = 0; hh < n_heads; ++hh) {
+        for (int f = 0; f < half; ++f) {
+            double sr = 0.0, si = 0.0, sn = 0.0;
+            for (int n = 0; n < n_cal; ++n) {
+                const size_t row = ((size_t)hh * n_cal + n) * d;
+                const double x = load_elem(q, dtype, row + f);
+                const double y = load_elem(q, dtype, row + f + half);
+                sr += x;
+                si += y;
+                sn += sqrt(x * x + y * y);
+            }
+            const double mr = sr / n_cal, mi = si / n_cal, mn = sn / n_cal;
+            qc_out[(size_t)hh * d + f] = mr;
+            qc_out[(size_t)hh * d + f + half] = mi;
+            qn_out[(size_t)hh * half + f] = mn;
+            r_out[(size_t)hh * half + f] = mn > 0.0 ? sqrt(mr * mr + mi * mi) / mn : 0.0;
+        }
+    }
+}
+
 /* Number of threads an OpenMP parallel region actually uses (for the CPU baseline record). */
 int oracle_max_threads(int n_threads)
 {

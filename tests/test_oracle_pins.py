@@ -401,3 +401,70 @@ def test_prune_streams_matches_per_step_calls(orc):
         _, F, _, _ = orc.zmax(raw)
         np.testing.assert_array_equal(res["F"][i], F)
         np.testing.assert_array_equal(res["kept"][i], orc.select(F, cfg.budget))
+
+
+# ---- calibration statistics ---------------------------------------------------------------------
+
+def test_calib_identical_queries_are_fully_concentrated(orc):
+    """Every captured query the same: the centre is that query, E|q_f| = |q_f| and R_f = 1."""
+    rng = np.random.default_rng(401)
+    q0 = rng.standard_normal(128).astype(np.float32)
+    q = np.tile(q0, (1, 1, 37, 1))
+    qc, qn, r = orc.calib_stats(q)
+    np.testing.assert_allclose(qc[0, 0], q0, rtol=1e-15)
+    np.testing.assert_allclose(qn[0, 0], np.hypot(q0[:64].astype(np.float64), q0[64:]), rtol=1e-14)
+    np.testing.assert_allclose(r[0, 0], 1.0, rtol=1e-14)
+
+
+def test_calib_unit_phasors_give_mean_resultant_length(orc):
+    """Unit-norm bands q_f = exp(i theta_n): E|q_f| = 1 and R_f is the mean resultant length
+    |mean_n exp(i theta_n)| of the phases (the unit-phasor definition of concentration,
+    chenxutan.com/d/2624 section 2.1), worked here with cmath on a small set."""
+    rng = np.random.default_rng(402)
+    n = 9
+    theta = rng.uniform(-math.pi, math.pi, (n, 64))
+    q = np.concatenate([np.cos(theta), np.sin(theta)], axis=1).astype(np.float32)
+    qc, qn, r = orc.calib_stats(q[None])
+    q64 = q.astype(np.float64)
+    for f in (0, 5, 63):
+        ph = [complex(q64[k, f], q64[k, f + 64]) for k in range(n)]
+        mrl = abs(sum(p / abs(p) for p in ph) / n)
+        assert abs(r[0, f] - mrl) < 1e-7          # |q_f| = 1 up to the fp32 rounding of cos/sin
+        assert abs(qn[0, f] - 1.0) < 1e-7
+
+
+def test_calib_symmetric_set_has_zero_centre(orc):
+    """Queries in opposite pairs (q and -q): the centre is exactly 0 and so is R."""
+    rng = np.random.default_rng(403)
+    a = rng.standard_normal((5, 128)).astype(np.float32)
+    q = np.concatenate([a, -a])[None, None]
+    qc, qn, r = orc.calib_stats(q)
+    assert np.all(qc == 0.0) and np.all(r == 0.0)
+    np.testing.assert_allclose(qn[0, 0], np.hypot(a[:, :64].astype(np.float64), a[:, 64:]).mean(axis=0),
+                               rtol=1e-14)
+
+
+def test_calib_invariants(orc):
+    """0 <= R_f <= 1 (triangle inequality); scaling every query by c > 0 scales the centre and
+    the mean norm by c and leaves R unchanged; a zero band has R = 0."""
+    rng = np.random.default_rng(404)
+    q = (rng.standard_normal((2, 3, 50, 128)) + 0.7).astype(np.float32)
+    q[1, 2, :, 7] = 0.0
+    q[1, 2, :, 71] = 0.0
+    qc, qn, r = orc.calib_stats(q)
+    assert np.all(r >= 0.0) and np.all(r <= 1.0 + 1e-15)
+    assert r[1, 2, 7] == 0.0 and qn[1, 2, 7] == 0.0
+    qc4, qn4, r4 = orc.calib_stats(q * np.float32(4.0))
+    np.testing.assert_allclose(qc4, 4.0 * qc, rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(qn4, 4.0 * qn, rtol=1e-14)
+    np.testing.assert_allclose(r4, r, rtol=1e-13)
+
+
+def test_calib_bf16_input_reads_exact_values(orc):
+    """bf16 captures are read exactly: the statistics equal those of the same values in fp32."""
+    rng = np.random.default_rng(405)
+    q32 = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((1, 2, 20, 128)).astype(np.float32)))
+    a = orc.calib_stats(synth.f32_to_bf16_bits(q32))
+    b = orc.calib_stats(q32)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
