@@ -12,6 +12,10 @@ kernels run on; the per-phase events (score / select / compact) give the dominan
 duration for the roofline.
 
 Prints one JSON line (see the keys below).  --gpus above 1 is refused: this path runs on one GPU.
+
+--workload calib measures instead the calibration-statistics kernel (tria_calib_stats) on the
+offline capture it would see for Qwen3-32B: 64 layers x 64 query heads x 10240 captured pre-RoPE
+queries in bf16 (about ten thousand calibration tokens), one launch per step.
 """
 from __future__ import annotations
 
@@ -72,6 +76,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--workload", choices=("prune", "calib"), default="prune",
+                    help="prune: the prune step (default); calib: calibration statistics of captured queries")
     ap.add_argument("--score-path", choices=("auto", "tiled"), default="auto",
                     help="long-stream bf16 scoring: auto (stream clusters keep raw scores on chip) or tiled")
     ap.add_argument("--variant", choices=VARIANTS, default="default",
@@ -106,6 +112,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     T.lib()   # fail loudly if the HIP library is missing
+    if args.workload == "calib":
+        return bench_calib(args, T, torch)
     T.set_score_path(T.PATH_TILED if args.score_path == "tiled" else T.PATH_AUTO)
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -231,6 +239,79 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3), pre_rope)
     calib.free()
+    print(json.dumps(out), flush=True)
+
+
+def bench_calib(args, T, torch):
+    """Calibration statistics over a captured-query tensor of Qwen3-32B shapes."""
+    L, Hq, n_cal, d = 64, 64, 10240, 128
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    # per head: centre of norm 8 plus N(0, s^2) noise, s ~ U(0.05, 3) (concentrated to diffuse)
+    centre = torch.randn((L, Hq, 1, d), generator=gen, device=dev)
+    centre = 8.0 * centre / centre.norm(dim=-1, keepdim=True)
+    spread = 0.05 + 2.95 * torch.rand((L, Hq, 1, 1), generator=gen, device=dev)
+    q = torch.empty((L, Hq, n_cal, d), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        q[l] = (centre[l] + spread[l] * torch.randn((Hq, n_cal, d), generator=gen, device=dev)).to(torch.bfloat16)
+    outs = (torch.empty((L, Hq, d), device=dev), torch.empty((L, Hq, d // 2), device=dev),
+            torch.empty((L, Hq, d // 2), device=dev))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        T.calib_stats(q, *outs, stream=stream)
+    torch.cuda.synchronize()
+    T.timing_read()
+    T.timing_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush.zero_()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        T.calib_stats(q, *outs, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    kern = T.timing_read()["calib"]
+    T.timing_enable(False)
+    ms = float(np.mean(times))
+    kms = kern["ms"] / max(kern["launches"], 1)
+    nbytes = L * Hq * n_cal * d * 2
+    out = {
+        "metric": "calibration queries/s (pre-RoPE query statistics)", "value": round(L * Hq * n_cal / (ms * 1e-3), 1),
+        "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3-32b-calibration-64layer-64qhead-10240q-bf16", "layers": L, "q_heads": Hq,
+                   "queries_per_head": n_cal, "head_dim": d},
+        "roofline": {"bound": "hbm", "kernel": "calib", "achieved": round(nbytes / (kms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic().get("calib")},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        oracle.build()
+
+        def run(n_layers):
+            qh = q[:n_layers].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            oracle.calib_stats(qh)
+            return time.perf_counter() - t0
+
+        n_layers = 1
+        dt = run(n_layers)
+        if dt < args.cpu_seconds / 2:
+            n_layers = int(min(16, max(1, args.cpu_seconds / max(dt, 1e-3))))
+            if n_layers > 1:
+                dt = run(n_layers)
+        n_heads = n_layers * Hq
+        out["cpu_baseline"] = {"value": round(n_heads * n_cal / dt, 1), "unit": "queries/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n_heads} of {L * Hq} heads ({n_heads * n_cal} queries), "
+                                                           f"fp64, single thread, {dt:.2f} s",
+                               "cpu": cpu_model()}
     print(json.dumps(out), flush=True)
 
 

@@ -149,6 +149,24 @@ tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void 
 const char *tria_status_string(tria_status status);
 
 /*
+ * Calibration statistics of captured pre-RoPE queries: the offline step that feeds
+ * tria_load_calib (chenxutan.com/d/2624 section 3.4; zhichai.net section "破局之道" for R;
+ * watermelonwater.tech "TriAttention 方案设计" item 1).  Per (layer, query head) and band f
+ * (q[f] + i q[f + head_dim/2]): qbar_f = mean_n q_{n,f}, E|q_f| = mean_n |q_{n,f}| and
+ * R_f = |qbar_f| / E|q_f| (0 when E|q_f| = 0).  Sums in fp64, in a fixed order (deterministic).
+ *   q            device [L][Hq][n_cal][head_dim] bf16 or fp32, half-split layout, 16-byte aligned
+ *   q_centre     device [L][Hq][head_dim] fp32 out
+ *   q_band_norm  device [L][Hq][head_dim/2] fp32 out
+ *   r_band       device [L][Hq][head_dim/2] fp32 out
+ * The outputs, copied to the host, are tria_load_calib's inputs.  Non-finite inputs give
+ * non-finite statistics (which tria_load_calib rejects).  Asynchronous on `stream`.
+ * Errors: INVALID (null pointer, n_cal < 1, bad sizes, misaligned), UNSUPPORTED (head_dim != 128),
+ * DEVICE (launch failure).
+ */
+tria_status tria_calib_stats(tria_dtype dtype, const void *q, int n_layers, int n_q_heads, int n_cal, int head_dim,
+                             float *q_centre, float *q_band_norm, float *r_band, void *stream);
+
+/*
  * Kernel timing (instrumentation, off by default).  While enabled, every timed kernel launched by
  * tria_score, tria_select_topB, tria_compact and tria_prune is bracketed by a pair of HIP events
  * recorded on the stream it runs on.  tria_timing_read waits for the recorded events, returns the
@@ -162,7 +180,8 @@ typedef enum {
     TRIA_TIMER_NORMALISE = 1,  /* per-head statistics, z-score and GQA max (long streams) */
     TRIA_TIMER_SELECT = 2,     /* top-B selection */
     TRIA_TIMER_COMPACT = 3,    /* in-place compaction */
-    TRIA_TIMER_COUNT = 4
+    TRIA_TIMER_CALIB = 4,      /* calibration statistics (tria_calib_stats) */
+    TRIA_TIMER_COUNT = 5
 } tria_timer;
 
 tria_status tria_timing_enable(int on);

@@ -27,9 +27,9 @@ EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
-    "tria_set_score_path",
+    "tria_set_score_path", "tria_calib_stats",
 )
-TIMERS = ("score_keys", "normalise", "select", "compact")
+TIMERS = ("score_keys", "normalise", "select", "compact", "calib")
 
 
 class TriaError(RuntimeError):
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.tria_timing_enable.argtypes = [I]
         L.tria_set_score_path.restype = I
         L.tria_set_score_path.argtypes = [I]
+        L.tria_calib_stats.restype = I
+        L.tria_calib_stats.argtypes = [I, P, I, I, I, I, P, P, P, P]
         L.tria_timing_read.restype = I
         L.tria_timing_read.argtypes = [ctypes.POINTER(D), ctypes.POINTER(I)]
         _lib = L
@@ -266,6 +268,24 @@ def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int
                           _stream(stream))
     _check(st, "tria_prune")
     return F, kept
+
+
+def calib_stats(q, q_centre=None, q_band_norm=None, r_band=None, stream=None):
+    """Calibration statistics of captured pre-RoPE queries q [L][Hq][n_cal][128] (bf16 or fp32)
+    on the device (``tria_calib_stats``): returns (q_centre [L][Hq][128], q_band_norm [L][Hq][64],
+    r_band [L][Hq][64]) float32 device tensors, the inputs of ``load_calib``."""
+    import torch
+    _dev(q, "q")
+    L, Hq, n_cal, d = q.shape
+    outs = []
+    for x, shape in ((q_centre, (L, Hq, d)), (q_band_norm, (L, Hq, d // 2)), (r_band, (L, Hq, d // 2))):
+        if x is None:
+            x = torch.empty(shape, dtype=torch.float32, device=q.device)
+        _dev(x, "output")
+        outs.append(x)
+    _check(lib().tria_calib_stats(_dtype_code(q), _ptr(q), L, Hq, n_cal, d, _ptr(outs[0]), _ptr(outs[1]),
+                                  _ptr(outs[2]), _stream(stream)), "tria_calib_stats")
+    return tuple(outs)
 
 
 PATH_AUTO = 0

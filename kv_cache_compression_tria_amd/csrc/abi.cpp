@@ -213,6 +213,20 @@ tria_status tria_score_check(const void *ws, size_t ws_bytes, void *stream)
     return flag ? TRIA_E_NONFINITE : TRIA_OK;
 }
 
+tria_status tria_calib_stats(tria_dtype dt, const void *q, int L, int Hq, int n_cal, int d, float *qc, float *qn,
+                             float *rb, void *stream)
+{
+    if (!q || !qc || !qn || !rb) return TRIA_E_INVALID;
+    if (dt != TRIA_BF16 && dt != TRIA_F32) return TRIA_E_INVALID;
+    if (L <= 0 || Hq <= 0 || n_cal <= 0) return TRIA_E_INVALID;
+    if ((long long)L * Hq > 0x7fffffffLL) return TRIA_E_INVALID;
+    if (d != TRIA_D) return TRIA_E_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(qc, 4) || !aligned(qn, 4) || !aligned(rb, 4)) return TRIA_E_INVALID;
+    if (tria::launch_calib_stats(dt, q, L * Hq, n_cal, qc, qn, rb, (hipStream_t)stream) != hipSuccess)
+        return TRIA_E_DEVICE;
+    return TRIA_OK;
+}
+
 tria_status tria_set_score_path(int path)
 {
     if (path != TRIA_PATH_AUTO && path != TRIA_PATH_TILED) return TRIA_E_INVALID;

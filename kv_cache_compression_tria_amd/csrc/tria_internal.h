@@ -86,6 +86,8 @@ hipError_t launch_tile_finish(int G, int streams, int N, const float *raw, const
 hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
                                const int32_t *t, int n_seq, int N, unsigned flags, float *F, float *raw_out,
                                float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+hipError_t launch_calib_stats(tria_dtype dt, const void *q, int n_heads, int n_cal, float *qc, float *qn, float *rb,
+                              hipStream_t st);
 hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
                        float *stats, hipStream_t st);
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st);
