@@ -13,6 +13,10 @@ duration for the roofline.
 
 Prints one JSON line (see the keys below).  --gpus above 1 is refused: this path runs on one GPU.
 
+--workload decode measures the decode loop on config 4 (Qwen3-8B shapes, 36 layers x 64
+sequences x 8 KV heads, B = 2048): one step appends the K/V rows of 128 new tokens to every
+stream and prunes the full cache (B + 128 rows) back to B (tria_decode_step).
+
 --workload calib measures instead the calibration-statistics kernel (tria_calib_stats) on the
 offline capture it would see for Qwen3-32B: 64 layers x 64 query heads x 10240 captured pre-RoPE
 queries in bf16 (about ten thousand calibration tokens), one launch per step.
@@ -76,8 +80,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
-    ap.add_argument("--workload", choices=("prune", "calib"), default="prune",
-                    help="prune: the prune step (default); calib: calibration statistics of captured queries")
+    ap.add_argument("--workload", choices=("prune", "decode", "calib"), default="prune",
+                    help="prune: the prune step (default); decode: append 128 tokens + prune per step; "
+                         "calib: calibration statistics of captured queries")
     ap.add_argument("--score-path", choices=("auto", "tiled"), default="auto",
                     help="long-stream bf16 scoring: auto (stream clusters keep raw scores on chip) or tiled")
     ap.add_argument("--variant", choices=VARIANTS, default="default",
@@ -114,6 +119,8 @@ def main():
     T.lib()   # fail loudly if the HIP library is missing
     if args.workload == "calib":
         return bench_calib(args, T, torch)
+    if args.workload == "decode":
+        return bench_decode(args, T, torch, synth)
     T.set_score_path(T.PATH_TILED if args.score_path == "tiled" else T.PATH_AUTO)
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -238,6 +245,75 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3), pre_rope)
+    calib.free()
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, T, torch, synth):
+    """Decode loop on config 4 shapes: append 128 tokens' rows, prune B + 128 -> B, per step."""
+    cfg = synth.CONFIGS[4]
+    dev = torch.device("cuda:0")
+    wl = synth.make_device(cfg, dev)             # N = B + 128 keys: a full cache
+    k, v, pos, t = wl["k"], wl["v"], wl["pos"], wl["t_dev"].clone()
+    S, L, Hkv, cap, d = k.shape
+    B = cfg.budget
+    n_new = cap - B
+    streams = S * L * Hkv
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], Hkv, cfg.theta)
+    # the rows of 128 new tokens (one draw, appended every step at advancing positions)
+    kn = k[:, :, :, B:].clone()
+    vn = v[:, :, :, B:].clone()
+    pn0 = pos[:, :, :, B:].clone()
+    F = torch.empty((S, L, Hkv, cap), dtype=torch.float32, device=dev)
+    kept = torch.empty((streams, B), dtype=torch.int32, device=dev)
+    ws = T.workspace(T.prune_workspace_bytes(calib, S, cap, B, k.dtype), dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    T.prune(calib, k, v, pos, t, B, F=F, kept=kept, ws=ws, stream=stream)    # start from a pruned cache
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    step_no = 0
+
+    def step():
+        nonlocal step_no
+        step_no += 1
+        pn = pn0 + 128 * step_no
+        t.add_(128)
+        return pn
+
+    for _ in range(args.warmup):
+        pn = step()
+        T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    T.timing_read()
+    T.timing_enable(True)
+    for _ in range(args.steps):
+        pn = step()
+        if not args.no_flush:
+            flush.zero_()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        n = T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        assert n == B
+        times.append(ev[0].elapsed_time(ev[1]))
+    kern = T.timing_read()
+    T.timing_enable(False)
+    T.score_check(ws)
+    ms = float(np.mean(times))
+    kernels = {name: {"avg_ms": round(kv["ms"] / kv["launches"], 4), "launches": kv["launches"]}
+               for name, kv in kern.items() if kv["launches"]}
+    out = {
+        "metric": "decode-loop keys/s (128 tokens appended, B+128 keys scored, selected, compacted)",
+        "value": round(streams * cap / (ms * 1e-3), 1), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name + "-decode-loop", "streams": streams, "capacity": cap, "budget": B,
+                   "new_tokens_per_step": n_new, "parallelism": "single-gpu"},
+        "generated_tokens_per_s": round(S * n_new / (ms * 1e-3), 1),
+        "kernels": kernels,
+    }
     calib.free()
     print(json.dumps(out), flush=True)
 

@@ -149,6 +149,36 @@ tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void 
 const char *tria_status_string(tria_status status);
 
 /*
+ * Decode loop (the cadence of the 10100.com article, section "TriAttention方法", and of
+ * watermelonwater.tech "TriAttention 方案设计" item 4: prune once every 128 generated tokens; the
+ * attention layer of chenxutan.com/d/2624 section 4 appends each token's K/V and prunes back to
+ * the budget).  The cache of every stream is a fixed-capacity buffer of `cap` rows (stream
+ * stride cap rows) of which the first `len` are live.
+ *
+ * tria_append: copy n_new rows per stream into rows [len, len + n_new) of K, V and pos.
+ *   k, v       device [S][L][Hkv][cap][head_dim] (bf16 or fp32), 16-byte aligned
+ *   pos        device [S][L][Hkv][cap] int32 (may be NULL)
+ *   k_new, v_new device [S][L][Hkv][n_new][head_dim], pos_new device [S][L][Hkv][n_new] (NULL iff
+ *              pos is NULL)
+ *   Errors: INVALID (null pointers, len < 0, n_new < 1, len + n_new > cap, misaligned),
+ *   UNSUPPORTED (head_dim != 128), DEVICE.
+ *
+ * tria_decode_step: tria_append, then, when the append fills the cache (len + n_new == cap) and
+ * cap > budget, tria_prune over the full cache (N = cap, t = position of each sequence's newest
+ * token) so that `budget` rows stay.  *new_len receives the live length afterwards (budget after
+ * a prune, else len + n_new).  F [S][L][Hkv][cap] and kept [streams][budget] are scratch outputs
+ * of the prune (valid when it ran); ws holds tria_prune_workspace_bytes(calib, dtype, n_seq, cap,
+ * budget).  Errors: those of tria_append and tria_prune.
+ */
+tria_status tria_append(tria_dtype dtype, void *k, void *v, int32_t *pos, int n_streams, int cap, int len,
+                        const void *k_new, const void *v_new, const int32_t *pos_new, int n_new, int head_dim,
+                        void *stream);
+tria_status tria_decode_step(const tria_calib *calib, tria_dtype dtype, void *k, void *v, int32_t *pos,
+                             const int32_t *t, int n_seq, int cap, int len, int budget, const void *k_new,
+                             const void *v_new, const int32_t *pos_new, int n_new, float *F, int32_t *kept,
+                             unsigned flags, void *ws, size_t ws_bytes, int *new_len, void *stream);
+
+/*
  * Calibration statistics of captured pre-RoPE queries: the offline step that feeds
  * tria_load_calib (chenxutan.com/d/2624 section 3.4; zhichai.net section "破局之道" for R;
  * watermelonwater.tech "TriAttention 方案设计" item 1).  Per (layer, query head) and band f

@@ -27,7 +27,7 @@ EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
-    "tria_set_score_path", "tria_calib_stats",
+    "tria_set_score_path", "tria_calib_stats", "tria_append", "tria_decode_step",
 )
 TIMERS = ("score_keys", "normalise", "select", "compact", "calib")
 
@@ -79,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.tria_set_score_path.restype = I
         L.tria_set_score_path.argtypes = [I]
         L.tria_calib_stats.restype = I
+        L.tria_append.restype = I
+        L.tria_append.argtypes = [I, P, P, P, I, I, I, P, P, P, I, I, P]
+        L.tria_decode_step.restype = I
+        L.tria_decode_step.argtypes = [P, I, P, P, P, P, I, I, I, I, P, P, P, I, P, P, U, P, S,
+                                       ctypes.POINTER(I), P]
         L.tria_calib_stats.argtypes = [I, P, I, I, I, I, P, P, P, P]
         L.tria_timing_read.restype = I
         L.tria_timing_read.argtypes = [ctypes.POINTER(D), ctypes.POINTER(I)]
@@ -286,6 +291,42 @@ def calib_stats(q, q_centre=None, q_band_norm=None, r_band=None, stream=None):
     _check(lib().tria_calib_stats(_dtype_code(q), _ptr(q), L, Hq, n_cal, d, _ptr(outs[0]), _ptr(outs[1]),
                                   _ptr(outs[2]), _stream(stream)), "tria_calib_stats")
     return tuple(outs)
+
+
+def append(k, v, pos, length: int, k_new, v_new, pos_new, stream=None):
+    """Copy the new rows k_new/v_new [S][L][Hkv][n][d] and pos_new [S][L][Hkv][n] into rows
+    [length, length + n) of the cache k/v [S][L][Hkv][cap][d], pos [S][L][Hkv][cap]
+    (``tria_append``)."""
+    S, L, Hkv, cap, d = k.shape
+    n = k_new.shape[-2]
+    for name, x in (("k", k), ("v", v), ("pos", pos), ("k_new", k_new), ("v_new", v_new), ("pos_new", pos_new)):
+        _dev(x, name)
+    _check(lib().tria_append(_dtype_code(k), _ptr(k), _ptr(v), _ptr(pos), S * L * Hkv, cap, int(length), _ptr(k_new),
+                             _ptr(v_new), _ptr(pos_new), n, d, _stream(stream)), "tria_append")
+
+
+def decode_step(calib: Calib, k, v, pos, t, length: int, budget: int, k_new, v_new, pos_new, F=None, kept=None,
+                flags: int = 0, ws=None, stream=None) -> int:
+    """Append the new rows and, when that fills the cache, prune it back to ``budget`` rows
+    (``tria_decode_step``).  Returns the live length afterwards."""
+    import torch
+    S, L, Hkv, cap, d = k.shape
+    n = k_new.shape[-2]
+    for name, x in (("k", k), ("v", v), ("pos", pos), ("t", t), ("k_new", k_new), ("v_new", v_new),
+                    ("pos_new", pos_new), ("F", F), ("kept", kept)):
+        _dev(x, name)
+    if F is None:
+        F = torch.empty((S, L, Hkv, cap), dtype=torch.float32, device=k.device)
+    if kept is None:
+        kept = torch.empty((S * L * Hkv, min(int(budget), cap)), dtype=torch.int32, device=k.device)
+    if ws is None:
+        ws = workspace(prune_workspace_bytes(calib, S, cap, budget, k.dtype), k.device)
+    out = ctypes.c_int(0)
+    _check(lib().tria_decode_step(calib.handle, _dtype_code(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(t), S, cap,
+                                  int(length), int(budget), _ptr(k_new), _ptr(v_new), _ptr(pos_new), n, _ptr(F),
+                                  _ptr(kept), int(flags), _ptr(ws), ws.numel() * ws.element_size(),
+                                  ctypes.byref(out), _stream(stream)), "tria_decode_step")
+    return out.value
 
 
 PATH_AUTO = 0

@@ -282,4 +282,39 @@ tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int
     return tria_compact(dt, k, v, pos, kept, n_streams, N, B, TRIA_D, stream);
 }
 
+tria_status tria_append(tria_dtype dt, void *k, void *v, int32_t *pos, int n_streams, int cap, int len,
+                        const void *kn, const void *vn, const int32_t *pn, int n_new, int d, void *stream)
+{
+    if (!k || !v || !kn || !vn || (pos == nullptr) != (pn == nullptr)) return TRIA_E_INVALID;
+    if (dt != TRIA_BF16 && dt != TRIA_F32) return TRIA_E_INVALID;
+    if (n_streams <= 0 || cap <= 0 || len < 0 || n_new < 1 || (long long)len + n_new > cap) return TRIA_E_INVALID;
+    if (d != TRIA_D) return TRIA_E_UNSUPPORTED;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kn, 16) || !aligned(vn, 16) || (pos && !aligned(pos, 4)) ||
+        (pn && !aligned(pn, 4)))
+        return TRIA_E_INVALID;
+    if (tria::launch_append(dt, k, v, pos, n_streams, cap, len, kn, vn, pn, n_new, (hipStream_t)stream) != hipSuccess)
+        return TRIA_E_DEVICE;
+    return TRIA_OK;
+}
+
+tria_status tria_decode_step(const tria_calib *c, tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *t,
+                             int n_seq, int cap, int len, int B, const void *kn, const void *vn, const int32_t *pn,
+                             int n_new, float *F, int32_t *kept, unsigned flags, void *ws, size_t ws_bytes,
+                             int *new_len, void *stream)
+{
+    if (!c || !new_len || B <= 0 || n_seq <= 0) return TRIA_E_INVALID;
+    if ((long long)n_seq * c->L * c->Hkv > 0x7fffffffLL) return TRIA_E_INVALID;
+    const int n_streams = n_seq * c->L * c->Hkv;
+    tria_status s = tria_append(dt, k, v, pos, n_streams, cap, len, kn, vn, pn, n_new, TRIA_D, stream);
+    if (s != TRIA_OK) return s;
+    if (len + n_new == cap && cap > B) {
+        s = tria_prune(c, dt, k, v, pos, t, n_seq, cap, B, F, kept, flags, ws, ws_bytes, stream);
+        if (s != TRIA_OK) return s;
+        *new_len = B;
+    } else {
+        *new_len = len + n_new;
+    }
+    return TRIA_OK;
+}
+
 }  // extern "C"

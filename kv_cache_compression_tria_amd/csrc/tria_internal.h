@@ -88,6 +88,8 @@ hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k
                                float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
 hipError_t launch_calib_stats(tria_dtype dt, const void *q, int n_heads, int n_cal, float *qc, float *qn, float *rb,
                               hipStream_t st);
+hipError_t launch_append(tria_dtype dt, void *k, void *v, int32_t *pos, int n_streams, int cap, int len,
+                         const void *kn, const void *vn, const int32_t *pn, int n_new, hipStream_t st);
 hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
                        float *stats, hipStream_t st);
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st);

@@ -110,11 +110,43 @@ def test_timing_api_without_pending_events(tria):
     """Timing can be switched on and off and read with nothing recorded (no GPU needed)."""
     T = tria
     L = T.lib()
-    ms = (ctypes.c_double * 4)()
-    n = (ctypes.c_int * 4)()
+    nt = len(T.TIMERS)                  # TRIA_TIMER_COUNT
+    ms = (ctypes.c_double * nt)()
+    n = (ctypes.c_int * nt)()
     assert L.tria_timing_enable(1) == T.OK
     assert L.tria_timing_read(ms, n) == T.OK
-    assert list(n) == [0, 0, 0, 0] and list(ms) == [0.0, 0.0, 0.0, 0.0]
+    assert list(n) == [0] * nt and list(ms) == [0.0] * nt
     assert L.tria_timing_enable(0) == T.OK
     assert L.tria_timing_read(None, n) == T.E_INVALID
     assert T.timing_read() == {name: {"ms": 0.0, "launches": 0} for name in T.TIMERS}
+
+
+def test_timer_names_match_header(tria):
+    """The binding names one timer per TRIA_TIMER_* slot (tria_timing_read writes COUNT entries)."""
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "tria.h")).read()
+    count = int(re.search(r"TRIA_TIMER_COUNT\s*=\s*(\d+)", text).group(1))
+    assert len(tria.TIMERS) == count
+
+
+def test_calib_append_decode_validation(tria):
+    """Argument errors of the calibration, append and decode-step entry points are reported
+    before any launch."""
+    L = tria.lib()
+    fake = ctypes.c_void_p(0x1000)
+    # tria_calib_stats(dtype, q, L, Hq, n_cal, d, qc, qn, rb, stream)
+    assert L.tria_calib_stats(0, None, 1, 1, 4, 128, fake, fake, fake, None) == tria.E_INVALID
+    assert L.tria_calib_stats(0, fake, 1, 1, 0, 128, fake, fake, fake, None) == tria.E_INVALID
+    assert L.tria_calib_stats(5, fake, 1, 1, 4, 128, fake, fake, fake, None) == tria.E_INVALID
+    assert L.tria_calib_stats(0, fake, 1, 1, 4, 64, fake, fake, fake, None) == tria.E_UNSUPPORTED
+    assert L.tria_calib_stats(0, ctypes.c_void_p(0x1008), 1, 1, 4, 128, fake, fake, fake, None) == tria.E_INVALID
+    # tria_append(dtype, k, v, pos, n_streams, cap, len, kn, vn, pn, n_new, d, stream)
+    assert L.tria_append(0, fake, fake, fake, 1, 16, 8, fake, fake, fake, 9, 128, None) == tria.E_INVALID   # overflow
+    assert L.tria_append(0, fake, fake, fake, 1, 16, -1, fake, fake, fake, 4, 128, None) == tria.E_INVALID
+    assert L.tria_append(0, fake, fake, fake, 1, 16, 0, fake, fake, fake, 0, 128, None) == tria.E_INVALID
+    assert L.tria_append(0, fake, fake, fake, 1, 16, 0, fake, fake, None, 4, 128, None) == tria.E_INVALID  # pos w/o pos_new
+    assert L.tria_append(0, fake, fake, None, 1, 16, 0, fake, fake, None, 4, 64, None) == tria.E_UNSUPPORTED
+    assert L.tria_append(0, ctypes.c_void_p(0x1004), fake, None, 1, 16, 0, fake, fake, None, 4, 128, None) == tria.E_INVALID
+    out = ctypes.c_int(-7)
+    assert L.tria_decode_step(None, 0, fake, fake, fake, fake, 1, 16, 0, 8, fake, fake, fake, 4, fake, fake, 0,
+                              fake, 1 << 20, ctypes.byref(out), None) == tria.E_INVALID
+    assert out.value == -7
