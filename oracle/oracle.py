@@ -44,7 +44,7 @@ def lib():
         L.oracle_omega.restype = D
         L.oracle_omega.argtypes = [D, I, I]
         L.oracle_score_stream.restype = None
-        L.oracle_score_stream.argtypes = [I, I, I, I, P, P, ctypes.c_int64, P, P, P, D, P, I, I, I, P, P, P]
+        L.oracle_score_stream.argtypes = [I, I, I, I, P, P, ctypes.c_int64, P, P, P, D, P, I, I, I, I, P, P, P]
         L.oracle_zmax.restype = I
         L.oracle_zmax.argtypes = [I, I, P, P, P, P, P]
         L.oracle_select.restype = I
@@ -52,7 +52,7 @@ def lib():
         L.oracle_compact_rows.restype = None
         L.oracle_compact_rows.argtypes = [I, ctypes.c_size_t, P, P]
         L.oracle_prune_streams.restype = I
-        L.oracle_prune_streams.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, D, P, I, I,
+        L.oracle_prune_streams.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, D, P, I, I,
                                            P, I, P, P, P, I]
         L.oracle_calib_stats.restype = None
         L.oracle_calib_stats.argtypes = [I, I, I, I, P, P, P, P]
@@ -78,7 +78,8 @@ def omega(theta: float, f: int, d: int) -> float:
     return lib().oracle_omega(theta, f, d)
 
 
-def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, form="lit", pre_rope=False):
+def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, form="lit", pre_rope=False,
+                 weight_r=False):
     """Raw scores of one stream.
 
     keys [N][d] (uint16 bf16 bits or float32; post-RoPE, or pre-RoPE with ``pre_rope``),
@@ -99,7 +100,8 @@ def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, f
     raw = np.zeros((G, N))
     lib().oracle_score_stream(N, d, G, _keys_dtype(keys), _ptr(keys), _ptr(pos), int(t), _ptr(qc),
                               _ptr(qn), _ptr(rb), float(theta), _ptr(off), len(off),
-                              0 if form == "lit" else 1, int(bool(pre_rope)), _ptr(st), _ptr(sn), _ptr(raw))
+                              0 if form == "lit" else 1, int(bool(pre_rope)), int(bool(weight_r)), _ptr(st),
+                              _ptr(sn), _ptr(raw))
     return st, sn, raw
 
 
@@ -138,11 +140,12 @@ def compact_rows(rows: np.ndarray, kept: np.ndarray) -> np.ndarray:
 
 
 def prune_streams(keys, pos, t, qc, qn, rb, B, n_kv_heads, stream_ids=None, theta=1e6,
-                  offsets=DEFAULT_OFFSETS, form="fac", want_raw=False, n_threads=0, pre_rope=False):
+                  offsets=DEFAULT_OFFSETS, form="fac", want_raw=False, n_threads=0, pre_rope=False, weight_r=False):
     """Oracle prune over a list of streams.
 
     keys [n][N][d] and pos [n][N] hold the listed streams (packed, in ``stream_ids`` order);
-    keys are post-RoPE, or the pre-RoPE bands themselves with ``pre_rope``;
+    keys are post-RoPE, or the pre-RoPE bands themselves with ``pre_rope``; ``weight_r`` weights
+    each band's trigonometric term by R_f;
     ``stream_ids`` are the global ids (s*L + l)*Hkv + g (default: 0..n-1).
     t [S], qc [L][Hq][d], qn/rb [L][Hq][d/2].
     Returns dict with F [n][N], kept [n][min(B,N)] and (optionally) raw [n][G][N].
@@ -171,7 +174,7 @@ def prune_streams(keys, pos, t, qc, qn, rb, B, n_kv_heads, stream_ids=None, thet
     qn_ = np.ascontiguousarray(qn, dtype=np.float32)
     rb_ = np.ascontiguousarray(rb, dtype=np.float32)
     off = np.ascontiguousarray(offsets, dtype=np.int64)
-    rc = lib().oracle_prune_streams(0 if form == "lit" else 1, int(bool(pre_rope)), _keys_dtype(keys), S, L, Hkv, G, N, d,
+    rc = lib().oracle_prune_streams(0 if form == "lit" else 1, int(bool(pre_rope)), int(bool(weight_r)), _keys_dtype(keys), S, L, Hkv, G, N, d,
                                     _ptr(keys), _ptr(pp), _ptr(tt), _ptr(qc_), _ptr(qn_), _ptr(rb_),
                                     float(theta), _ptr(off), len(off), int(B), _ptr(ids), n,
                                     _ptr(F), _ptr(raw), _ptr(kept), int(n_threads))

@@ -89,11 +89,14 @@ static double load_elem(const void *base, int dtype, size_t idx)
  *   off    : [n_off]   future offsets D
  *   form   : 0 = lit, 1 = fac
  *   pre_rope: 0 = keys are post-RoPE (ktilde), 1 = keys are the pre-RoPE bands k_f themselves
- * Outputs (each [G][N], any may be NULL): s_trig, s_norm, raw = s_trig + s_norm.
+ *   weight_r: 0 = s = S_trig + S_norm; 1 = the trigonometric term of band f is weighted by R_f,
+ *             s = sum_f R_f * (band f of S_trig) + S_norm, the convex R / (1 - R) mix of zhichai.net
+ *             section "TriAttention：把理论变成算法" item 3 taken per band
+ * Outputs (each [G][N], any may be NULL): s_trig (R-weighted with weight_r), s_norm, raw = s_trig + s_norm.
  */
 void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const int32_t *pos,
                          int64_t t, const float *qc, const float *qn, const float *rb,
-                         double theta, const int64_t *off, int n_off, int form, int pre_rope,
+                         double theta, const int64_t *off, int n_off, int form, int pre_rope, int weight_r,
                          double *s_trig, double *s_norm, double *raw)
 {
     const int half = d / 2;
@@ -136,7 +139,8 @@ void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const
                         double qmag = sqrt(qr * qr + qi * qi);
                         double qarg = atan2(qi, qr);
                         double dist = (double)(t + off[m]) - p;
-                        acc += qmag * kmag[f] * cos(w[f] * dist + qarg - karg[f]);
+                        double wr = weight_r ? (double)rb[(size_t)h * half + f] : 1.0;
+                        acc += wr * qmag * kmag[f] * cos(w[f] * dist + qarg - karg[f]);
                     }
                     trig += acc;
                 }
@@ -147,7 +151,8 @@ void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const
                     double qmag = sqrt(qr * qr + qi * qi);
                     double qarg = atan2(qi, qr);
                     double A = w[f] * ((double)t - p) + qarg - karg[f];
-                    trig += qmag * kmag[f] * (Cf[f] * cos(A) - Sf[f] * sin(A));
+                    double wr = weight_r ? (double)rb[(size_t)h * half + f] : 1.0;
+                    trig += wr * qmag * kmag[f] * (Cf[f] * cos(A) - Sf[f] * sin(A));
                 }
             }
             for (int f = 0; f < half; ++f)
@@ -253,7 +258,7 @@ void oracle_compact_rows(int nk, size_t row_bytes, unsigned char *rows, const in
  * kept_out [n_idx][min(B,N)] (may be NULL).
  * Returns 0, or -1 if a non-finite score was met.
  */
-int oracle_prune_streams(int form, int pre_rope, int dtype, int S, int L, int Hkv, int G, int N, int d,
+int oracle_prune_streams(int form, int pre_rope, int weight_r, int dtype, int S, int L, int Hkv, int G, int N, int d,
                          const void *keys, const int32_t *pos, const int64_t *t,
                          const float *qc, const float *qn, const float *rb, double theta,
                          const int64_t *off, int n_off, int B,
@@ -281,7 +286,7 @@ int oracle_prune_streams(int form, int pre_rope, int dtype, int S, int L, int Hk
         double *raw = raw_out ? raw_out + (size_t)i * G * N : (double *)malloc(sizeof(double) * (size_t)G * N);
         double *F = F_out ? F_out + (size_t)i * N : (double *)malloc(sizeof(double) * (size_t)N);
         oracle_score_stream(N, d, G, dtype, kb, pb, t[s], qc + h0 * d, qn + h0 * half, rb + h0 * half,
-                            theta, off, n_off, form, pre_rope, NULL, NULL, raw);
+                            theta, off, n_off, form, pre_rope, weight_r, NULL, NULL, raw);
         int rc = oracle_zmax(N, G, raw, NULL, F, NULL, NULL);
         if (rc == 0 && kept_out) rc = oracle_select(N, B, F, kept_out + (size_t)i * nk) < 0 ? -1 : 0;
         if (rc != 0) bad |= 1;

@@ -468,3 +468,49 @@ def test_calib_bf16_input_reads_exact_values(orc):
     b = orc.calib_stats(q32)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ---- P12: the R-weighted trigonometric term ------------------------------------------------------
+
+def test_p12_weight_r_limits(orc):
+    """R = 1 in every band: the weighted form equals the plain one (no norm term either); R = 0:
+    the trigonometric part vanishes and the score is the norm score sum_f E|q_f| |k_f|."""
+    rng = np.random.default_rng(120)
+    keys, pos, qc, qn, _ = rand_stream(rng, 40, 128, 3, 9000, "bf16")
+    ones = np.ones((3, 64), np.float32)
+    a = orc.score_stream(keys, pos, 9000, qc, qn, ones, form="fac", weight_r=True)
+    b = orc.score_stream(keys, pos, 9000, qc, qn, ones, form="fac")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    zeros = np.zeros((3, 64), np.float32)
+    st, sn, raw = orc.score_stream(keys, pos, 9000, qc, qn, zeros, form="lit", weight_r=True)
+    assert np.all(st == 0.0)
+    kt = keys_f64(keys)
+    mag = np.hypot(kt[:, :64], kt[:, 64:])
+    np.testing.assert_allclose(raw, qn.astype(np.float64) @ mag.T, rtol=1e-13)
+
+
+@pytest.mark.parametrize("form", ["lit", "fac"])
+def test_p12_weight_r_single_band_closed_form(orc, form):
+    """One band with R_f = 0.3: s = 0.3 |q||k| mean_d cos(w_f (t+d-p) + arg q - arg k)
+    + 0.7 E|q_f| |k_f|, worked with cmath."""
+    d, t, f = 128, 4000, 11
+    w = synth.omega_table(d)
+    qc = np.zeros((1, d), np.float32)
+    qc[0, f], qc[0, f + 64] = 1.5, -0.25
+    post = np.zeros((2, d), np.float32)
+    post[:, f] = [0.75, -2.0]
+    post[:, f + 64] = [1.25, 0.5]
+    pos = np.array([100, 3900], np.int32)
+    qn = np.full((1, 64), 2.5, np.float32)
+    rb = np.full((1, 64), 0.3, np.float32)
+    _, _, raw = orc.score_stream(post, pos, t, qc, qn, rb, form=form, weight_r=True)
+    q = complex(1.5, -0.25)
+    R = float(np.float32(0.3))
+    for j in range(2):
+        kt = complex(float(post[j, f]), float(post[j, f + 64]))
+        k = kt * complex(math.cos(w[f] * pos[j]), -math.sin(w[f] * pos[j]))
+        trig = sum(abs(q) * abs(k) * math.cos(w[f] * (t + dd - int(pos[j])) + math.atan2(q.imag, q.real)
+                                              - math.atan2(k.imag, k.real)) for dd in D_DEF) / len(D_DEF)
+        val = R * trig + (1 - R) * 2.5 * abs(k)
+        assert abs(raw[0, j] - val) < 1e-12 * (abs(q) * abs(k) + 2.5 * abs(k))
