@@ -61,6 +61,10 @@ typedef enum { TRIA_BF16 = 0, TRIA_F32 = 1 } tria_dtype;
                                  in the literal per-key form; same result, more arithmetic. */
 #define TRIA_KEYS_PRE_ROPE 2u /* keys are stored before RoPE (k_f, not k_f*exp(i w_f p)); the
                                  score then needs each key's distance phase w_f*(t-p_j). */
+#define TRIA_TRIG_WEIGHT_R 4u /* weight band f of the trigonometric series by R_f: the R / (1 - R)
+                                 mix of zhichai.net section "TriAttention：把理论变成算法" item 3,
+                                 per band (the norm term keeps its (1 - R_f) weight).  Not
+                                 combined with the two flags above (TRIA_E_UNSUPPORTED). */
 
 typedef struct tria_calib tria_calib; /* opaque, library-owned, immutable after load */
 

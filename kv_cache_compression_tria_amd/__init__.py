@@ -22,6 +22,7 @@ OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_NONFINITE, E_WORKSPACE = 0, -
 BF16, F32 = 0, 1
 PER_KEY_PHASE = 1
 KEYS_PRE_ROPE = 2
+TRIG_WEIGHT_R = 4
 
 EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",

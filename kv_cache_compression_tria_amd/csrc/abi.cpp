@@ -122,7 +122,8 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     const size_t bW = tria::align256(sizeof(float) * W.size());
     const size_t bnu = tria::align256(sizeof(uint64_t) * TRIA_HALF);
     const size_t bPW = tria::align256(sizeof(float) * PW.size());
-    c->block_bytes = bP + bP32 + bW + bnu + bPW;
+    const size_t bR = tria::align256(sizeof(float) * nh * TRIA_HALF);
+    c->block_bytes = bP + bP32 + bW + bnu + bPW + bR;
     if (hipMalloc(&c->block, c->block_bytes) != hipSuccess) { delete c; return TRIA_E_NOMEM; }
     char *b = (char *)c->block;
     c->P = (double2 *)b;
@@ -130,6 +131,7 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     c->W = (float *)(b + bP + bP32);
     c->nu = (uint64_t *)(b + bP + bP32 + bW);
     c->PW = (float *)(b + bP + bP32 + bW + bnu);
+    c->R = (float *)(b + bP + bP32 + bW + bnu + bPW);
     hipStream_t st = (hipStream_t)stream;
     bool ok = hipStreamSynchronize(st) == hipSuccess;
     ok = ok && hipMemcpy(c->P, P.data(), sizeof(double2) * P.size(), hipMemcpyHostToDevice) == hipSuccess;
@@ -137,6 +139,7 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     ok = ok && hipMemcpy(c->W, W.data(), sizeof(float) * W.size(), hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->nu, nu.data(), sizeof(uint64_t) * TRIA_HALF, hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->PW, PW.data(), sizeof(float) * PW.size(), hipMemcpyHostToDevice) == hipSuccess;
+    ok = ok && hipMemcpy(c->R, rb, sizeof(float) * nh * TRIA_HALF, hipMemcpyHostToDevice) == hipSuccess;
     if (!ok) {
         (void)hipFree(c->block);
         delete c;
@@ -179,7 +182,8 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     if (!c || !k || !t || !F) return TRIA_E_INVALID;
     if (dt != TRIA_BF16 && dt != TRIA_F32) return TRIA_E_INVALID;
     if (n_seq <= 0 || N <= 0 || N > (1 << 24)) return TRIA_E_INVALID;
-    if ((flags & ~(TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0) return TRIA_E_INVALID;
+    if ((flags & ~(TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE | TRIA_TRIG_WEIGHT_R)) != 0) return TRIA_E_INVALID;
+    if ((flags & TRIA_TRIG_WEIGHT_R) && (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE))) return TRIA_E_UNSUPPORTED;
     if ((flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) && !pos) return TRIA_E_INVALID;
     if ((size_t)n_seq * c->L * c->Hkv > (size_t)0x7fffffff) return TRIA_E_INVALID;
     if (!aligned(k, 16) || !aligned(F, 4) || (raw && !aligned(raw, 4)) || (stats && !aligned(stats, 4)) ||
@@ -193,7 +197,8 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     char *w = (char *)ws;
     float *qrot = (float *)(w + lay.qrot_off);
     // the rotation kernel also clears the non-finite flag (no memset node: safe under graph capture)
-    if (tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), st) != hipSuccess)
+    if (tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), (flags & TRIA_TRIG_WEIGHT_R) != 0, st) !=
+        hipSuccess)
         return TRIA_E_DEVICE;
     if (tria::launch_score(c, dt, k, pos, t, n_seq, N, qrot, F, raw, stats, flags, lay, w, st) != hipSuccess)
         return TRIA_E_DEVICE;

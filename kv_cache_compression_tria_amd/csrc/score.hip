@@ -65,11 +65,13 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
 
 // ---- a2: rotated queries --------------------------------------------------------------------
 // qrot[s][l][h][f] = Re Q_f, qrot[..][64+f] = Im Q_f with Q_f = P_f * exp(i w_f t_s) and
-// P_f = qbar_f * mean_d exp(i w_f d) precomputed in fp64 at table load.
+// P_f = qbar_f * mean_d exp(i w_f d) precomputed in fp64 at table load; with R (the
+// R-weighted variant) Q_f is scaled by R_f.
 __global__ __launch_bounds__(256) void rotate_queries_kernel(const double2 *__restrict__ P,
                                                              const uint64_t *__restrict__ nu,
                                                              const int32_t *__restrict__ t, int LHq,
-                                                             int total, float *__restrict__ qrot,
+                                                             int total, const float *__restrict__ R,
+                                                             float *__restrict__ qrot,
                                                              int *__restrict__ err)
 {
     // clear the non-finite flag of this call (no memset node)
@@ -85,15 +87,18 @@ __global__ __launch_bounds__(256) void rotate_queries_kernel(const double2 *__re
     double sn, cs;
     sincospi(2.0 * r, &sn, &cs);
     const double2 p = P[(size_t)lh * TRIA_HALF + f];
-    qrot[(size_t)gh * TRIA_D + f] = (float)(p.x * cs - p.y * sn);
-    qrot[(size_t)gh * TRIA_D + TRIA_HALF + f] = (float)(p.x * sn + p.y * cs);
+    const double wr = R ? (double)R[(size_t)lh * TRIA_HALF + f] : 1.0;
+    qrot[(size_t)gh * TRIA_D + f] = (float)(wr * (p.x * cs - p.y * sn));
+    qrot[(size_t)gh * TRIA_D + TRIA_HALF + f] = (float)(wr * (p.x * sn + p.y * cs));
 }
 
-hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, hipStream_t st)
+hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, bool weight_r,
+                         hipStream_t st)
 {
     const int total = n_seq * c->L * c->Hq;
     const int LHq = c->L * c->Hq;
-    rotate_queries_kernel<<<(total + 3) / 4, 256, 0, st>>>(c->P, c->nu, t, LHq, total, qrot, err);
+    rotate_queries_kernel<<<(total + 3) / 4, 256, 0, st>>>(c->P, c->nu, t, LHq, total, weight_r ? c->R : nullptr,
+                                                           qrot, err);
     return hipGetLastError();
 }
 
@@ -495,7 +500,8 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
-    if (flags != 0) return launch_score_perkey(c, dt, k, pos, t, n_seq, N, flags, F, raw, stats, lay, ws, st);
+    if (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE))
+        return launch_score_perkey(c, dt, k, pos, t, n_seq, N, flags, F, raw, stats, lay, ws, st);
     // bf16 caches score on the matrix cores; fp32 caches on the vector ALU
     return dt == TRIA_BF16 ? launch_score_mfma(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st)
                            : launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);

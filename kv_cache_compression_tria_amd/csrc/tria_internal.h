@@ -26,6 +26,7 @@ struct tria_calib {
     float *W;        // [L][Hq][64] norm weights (1 - R_f) E|q_f|
     uint64_t *nu;    // [64] w_f / (2 pi) as a 64-bit fraction of a turn
     float *PW;       // [L][Hkv][64][3][G] Re P32, Im P32 and W of each KV group, band-major
+    float *R;        // [L][Hq][64] R_f (the weight of the trigonometric term under TRIA_TRIG_WEIGHT_R)
 };
 
 // Workspace layout of tria_score (every region 256-byte aligned).
@@ -71,7 +72,8 @@ class KernelTimer {
 tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys);
 
 // kernel launchers (return hipSuccess or the launch error)
-hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, hipStream_t st);
+hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, bool weight_r,
+                         hipStream_t st);
 hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st);

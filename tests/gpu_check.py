@@ -115,6 +115,7 @@ def variant(base: int, **kw):
 def run_case(orc, T, cfg, form="fac", sample=None, flags=0):
     print(f"\n[case] {cfg.describe()} form={form} flags={flags}", flush=True)
     pre_rope = bool(flags & T.KEYS_PRE_ROPE)
+    weight_r = bool(flags & T.TRIG_WEIGHT_R)
     wl = synth.make_host(cfg, pre_rope=pre_rope)
     dev = synth.to_device(wl)
     calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
@@ -123,7 +124,7 @@ def run_case(orc, T, cfg, form="fac", sample=None, flags=0):
     out = gpu_prune(T, calib, dev, B, flags=flags)
     ids = np.arange(cfg.n_streams) if sample is None else np.asarray(sample)
     res = orc.prune_streams(kb[ids], pb[ids], wl["t"], wl["qc"], wl["qn"], wl["rb"], B, cfg.n_kv_heads,
-                            stream_ids=ids, form=form, want_raw=True, pre_rope=pre_rope)
+                            stream_ids=ids, form=form, want_raw=True, pre_rope=pre_rope, weight_r=weight_r)
     e_raw = check_raw(out["raw"][ids], res["raw"])
     e_F = check_F(out["F"][ids], res["F"])
     n_diff = check_kept_sets(out["kept"][ids], res["kept"], res["F"], B)

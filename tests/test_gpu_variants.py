@@ -106,3 +106,37 @@ def test_variant_requires_positions(T):
     with pytest.raises(T.TriaError):
         T.score(calib, dev["k"], dev["t_dev"], flags=T.PER_KEY_PHASE)
     calib.free()
+
+
+# ---- R-weighted trigonometric term (TRIA_TRIG_WEIGHT_R) -------------------------------------------
+
+def test_weight_r_config2_literal_oracle(orc, T):
+    """Raw scores kept on chip (one block per stream), bf16."""
+    gc.run_case(orc, T, synth.CONFIGS[2], form="lit", flags=T.TRIG_WEIGHT_R)
+
+
+def test_weight_r_config1_fp32(orc, T):
+    """fp32 cache: the vector-ALU scorer."""
+    gc.run_case(orc, T, synth.CONFIGS[1], form="lit", flags=T.TRIG_WEIGHT_R)
+
+
+@pytest.mark.parametrize("G,dtype,N", [(8, "bf16", 5000), (3, "f32", 7000), (2, "bf16", 70001)])
+def test_weight_r_long_streams(orc, T, G, dtype, N):
+    """Long streams: stream clusters (bf16) and the tiled vector path (fp32)."""
+    cfg = gc.variant(2, name=f"wr-g{G}-{dtype}-N{N}", n_q_heads=G, n_kv_heads=1, n_seq=2, n_keys=N,
+                     budget=N // 3 + 7, dtype=dtype, t_fixed=N + 1000, calib="head_r", r_range=(0.3, 0.99),
+                     seed=350 + G)
+    gc.run_case(orc, T, cfg, flags=T.TRIG_WEIGHT_R)
+
+
+def test_weight_r_with_per_key_flags_is_unsupported(T):
+    cfg = gc.variant(2, name="wr-unsup", n_q_heads=4, n_kv_heads=1, n_keys=64, budget=8, seed=360,
+                     positions="contiguous")
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1)
+    for extra in (T.PER_KEY_PHASE, T.KEYS_PRE_ROPE):
+        with pytest.raises(T.TriaError) as e:
+            T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=T.TRIG_WEIGHT_R | extra)
+        assert e.value.status == T.E_UNSUPPORTED
+    calib.free()
