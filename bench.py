@@ -196,8 +196,10 @@ def main():
     alg = synth.algorithmic_bytes(cfg, moved)
     r = d * cfg.elem_bytes
     # algorithmic bytes per launch of each timed kernel (what the method must move, no overheads)
+    # on the stream-cluster path the scoring kernel also writes F (no separate normaliser)
+    on_chip_finish = kern["normalise"]["launches"] == 0
     kern_bytes = {
-        "score_keys": n_streams * N * r,        # every cached key read once
+        "score_keys": n_streams * N * r + (n_streams * N * 4 if on_chip_finish else 0),   # keys read once (+ F)
         "normalise": n_streams * N * 4,         # F written once
         "select": n_streams * N * 4,            # F read once
         "compact": moved * (4 * r + 8),         # moved K, V rows and positions, read + written
