@@ -17,6 +17,7 @@ _SRC = os.path.join(_HERE, "tria_oracle.c")
 _LIB = os.path.join(_HERE, "libtria_oracle.so")
 
 DEFAULT_OFFSETS = tuple(2 ** i for i in range(17))  # D = {1, 2, 4, ..., 2^16}
+_FORMS = {"lit": 0, "fac": 1, "max": 2}            # offset mean (literal / factored), offset max
 
 
 def build(force: bool = False) -> str:
@@ -100,7 +101,7 @@ def score_stream(keys, pos, t, qc, qn, rb, theta=1e6, offsets=DEFAULT_OFFSETS, f
     raw = np.zeros((G, N))
     lib().oracle_score_stream(N, d, G, _keys_dtype(keys), _ptr(keys), _ptr(pos), int(t), _ptr(qc),
                               _ptr(qn), _ptr(rb), float(theta), _ptr(off), len(off),
-                              0 if form == "lit" else 1, int(bool(pre_rope)), int(bool(weight_r)), _ptr(st),
+                              _FORMS[form], int(bool(pre_rope)), int(bool(weight_r)), _ptr(st),
                               _ptr(sn), _ptr(raw))
     return st, sn, raw
 
@@ -174,7 +175,7 @@ def prune_streams(keys, pos, t, qc, qn, rb, B, n_kv_heads, stream_ids=None, thet
     qn_ = np.ascontiguousarray(qn, dtype=np.float32)
     rb_ = np.ascontiguousarray(rb, dtype=np.float32)
     off = np.ascontiguousarray(offsets, dtype=np.int64)
-    rc = lib().oracle_prune_streams(0 if form == "lit" else 1, int(bool(pre_rope)), int(bool(weight_r)), _keys_dtype(keys), S, L, Hkv, G, N, d,
+    rc = lib().oracle_prune_streams(_FORMS[form], int(bool(pre_rope)), int(bool(weight_r)), _keys_dtype(keys), S, L, Hkv, G, N, d,
                                     _ptr(keys), _ptr(pp), _ptr(tt), _ptr(qc_), _ptr(qn_), _ptr(rb_),
                                     float(theta), _ptr(off), len(off), int(B), _ptr(ids), n,
                                     _ptr(F), _ptr(raw), _ptr(kept), int(n_threads))

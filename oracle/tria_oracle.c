@@ -87,7 +87,9 @@ static double load_elem(const void *base, int dtype, size_t idx)
  *   qn     : [G][d/2]  E|q_f|
  *   rb     : [G][d/2]  R_f
  *   off    : [n_off]   future offsets D
- *   form   : 0 = lit, 1 = fac
+ *   form   : 0 = lit, 1 = fac, 2 = max: the largest of the per-offset series instead of their mean
+ *            (chenxutan.com/d/2624 section 3.3: the final trigonometric score is the maximum over
+ *            the offsets; evaluated literally, offset by offset)
  *   pre_rope: 0 = keys are post-RoPE (ktilde), 1 = keys are the pre-RoPE bands k_f themselves
  *   weight_r: 0 = s = S_trig + S_norm; 1 = the trigonometric term of band f is weighted by R_f,
  *             s = sum_f R_f * (band f of S_trig) + S_norm, the convex R / (1 - R) mix of zhichai.net
@@ -131,7 +133,7 @@ void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const
         for (int h = 0; h < G; ++h) {
             const float *q = qc + (size_t)h * d;
             double trig = 0.0, nrm = 0.0;
-            if (form == 0) {
+            if (form == 0 || form == 2) {
                 for (int m = 0; m < n_off; ++m) {
                     double acc = 0.0;
                     for (int f = 0; f < half; ++f) {
@@ -142,9 +144,12 @@ void oracle_score_stream(int N, int d, int G, int dtype, const void *keys, const
                         double wr = weight_r ? (double)rb[(size_t)h * half + f] : 1.0;
                         acc += wr * qmag * kmag[f] * cos(w[f] * dist + qarg - karg[f]);
                     }
-                    trig += acc;
+                    if (form == 0)
+                        trig += acc;
+                    else
+                        trig = (m == 0 || acc > trig) ? acc : trig;
                 }
-                trig /= n_off;
+                if (form == 0) trig /= n_off;
             } else {
                 for (int f = 0; f < half; ++f) {
                     double qr = q[f], qi = q[f + half];

@@ -514,3 +514,56 @@ def test_p12_weight_r_single_band_closed_form(orc, form):
                                               - math.atan2(k.imag, k.real)) for dd in D_DEF) / len(D_DEF)
         val = R * trig + (1 - R) * 2.5 * abs(k)
         assert abs(raw[0, j] - val) < 1e-12 * (abs(q) * abs(k) + 2.5 * abs(k))
+
+
+# ---- P13: the maximum over the future offsets ----------------------------------------------------
+
+def test_p13_max_over_one_offset_is_the_plain_score(orc):
+    """D with a single offset: the maximum and the mean are the same number."""
+    rng = np.random.default_rng(130)
+    keys, pos, qc, qn, rb = rand_stream(rng, 30, 128, 3, 7000, "bf16")
+    for dd in (0, 1, 4096):
+        a = orc.score_stream(keys, pos, 7000, qc, qn, rb, offsets=(dd,), form="max")
+        b = orc.score_stream(keys, pos, 7000, qc, qn, rb, offsets=(dd,), form="lit")
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def test_p13_max_is_the_largest_per_offset_rope_dot(orc):
+    """The max form equals the largest over d of <RoPE(qbar, t+d), ktilde_j> (numpy fp64 RoPE) when
+    the query equals its centre, and it is never below the offset mean."""
+    rng = np.random.default_rng(131)
+    d, G, N, t = 128, 2, 25, 12000
+    keys, pos, qc, qn, rb = rand_stream(rng, N, d, G, t, "f32")
+    w = synth.omega_table(d)
+    kt = keys_f64(keys)
+    st, _, _ = orc.score_stream(keys, pos, t, qc, qn, rb, form="max")
+    per = np.stack([np_rope(qc.astype(np.float64), t + dd, w) @ kt.T for dd in D_DEF])
+    expect = per.max(axis=0)
+    scale = np.abs(np_rope(qc.astype(np.float64), t, w)) @ np.abs(kt).T
+    assert np.max(np.abs(st - expect) / scale) < 1e-11
+    mean, _, _ = orc.score_stream(keys, pos, t, qc, qn, rb, form="lit")
+    assert np.all(st >= mean - 1e-9 * scale)
+
+
+def test_p13_max_single_band_closed_form(orc):
+    """One band: max_d |q||k| cos(w_f (t+d-p) + arg q - arg k) + the norm term, with cmath."""
+    d, t, f = 128, 5000, 3
+    w = synth.omega_table(d)
+    qc = np.zeros((1, d), np.float32)
+    qc[0, f], qc[0, f + 64] = -1.0, 0.5
+    post = np.zeros((2, d), np.float32)
+    post[:, f] = [1.5, -0.25]
+    post[:, f + 64] = [0.5, 2.0]
+    pos = np.array([7, 4990], np.int32)
+    qn = np.full((1, 64), 1.25, np.float32)
+    rb = np.full((1, 64), 0.75, np.float32)
+    _, _, raw = orc.score_stream(post, pos, t, qc, qn, rb, form="max")
+    q = complex(-1.0, 0.5)
+    for j in range(2):
+        kt = complex(float(post[j, f]), float(post[j, f + 64]))
+        k = kt * complex(math.cos(w[f] * pos[j]), -math.sin(w[f] * pos[j]))
+        trig = max(abs(q) * abs(k) * math.cos(w[f] * (t + dd - int(pos[j])) + math.atan2(q.imag, q.real)
+                                              - math.atan2(k.imag, k.real)) for dd in D_DEF)
+        val = trig + (1 - float(np.float32(0.75))) * 1.25 * abs(k)
+        assert abs(raw[0, j] - val) < 1e-12 * (abs(q) * abs(k) + abs(k))
