@@ -68,7 +68,7 @@ def measured_traffic() -> dict:
     return out
 
 
-VARIANTS = ("default", "per_key_phase", "pre_rope")
+VARIANTS = ("default", "per_key_phase", "pre_rope", "weight_r", "offset_max")
 
 
 def parse():
@@ -87,7 +87,8 @@ def parse():
                     help="long-stream bf16 scoring: auto (stream clusters keep raw scores on chip) or tiled")
     ap.add_argument("--variant", choices=VARIANTS, default="default",
                     help="scoring form: default (post-RoPE keys, rotated queries), per_key_phase (post-RoPE "
-                         "keys, literal per-key phases), pre_rope (keys cached before RoPE)")
+                         "keys, literal per-key phases), pre_rope (keys cached before RoPE), weight_r (R-weighted "
+                         "trigonometric term), offset_max (maximum over the future offsets)")
     return ap.parse_args()
 
 
@@ -126,7 +127,8 @@ def main():
     dev = torch.device("cuda:0")
     t0 = time.time()
     pre_rope = args.variant == "pre_rope"
-    flags = {"default": 0, "per_key_phase": T.PER_KEY_PHASE, "pre_rope": T.KEYS_PRE_ROPE}[args.variant]
+    flags = {"default": 0, "per_key_phase": T.PER_KEY_PHASE, "pre_rope": T.KEYS_PRE_ROPE,
+             "weight_r": T.TRIG_WEIGHT_R, "offset_max": T.OFFSET_MAX}[args.variant]
     if args.config >= 4:
         wl = synth.make_device(cfg, dev, pre_rope=pre_rope)
     else:
@@ -159,7 +161,7 @@ def main():
 
     def step():
         ev[0].record(stream)
-        T.score(calib, k, t, F=F, ws=ws, stream=stream, pos=pos if flags else None, flags=flags)
+        T.score(calib, k, t, F=F, ws=ws, stream=stream, pos=pos if flags & 3 else None, flags=flags)
         ev[1].record(stream)
         T.select_topB(F, B, kept=kept, stream=stream)
         ev[2].record(stream)
@@ -246,7 +248,9 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3), pre_rope)
+        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3), pre_rope,
+                                           form="max" if args.variant == "offset_max" else "fac",
+                                           weight_r=args.variant == "weight_r")
     calib.free()
     print(json.dumps(out), flush=True)
 
@@ -393,7 +397,7 @@ def bench_calib(args, T, torch):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False):
+def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False, form="fac", weight_r=False):
     """The fp64 oracle (factored form, OpenMP over streams) on a bounded sample of streams of the
     same workload, timed on the host cores."""
     import synth
@@ -410,7 +414,7 @@ def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False):
         ph = pp[ids[0]:ids[-1] + 1].cpu().numpy()
         t0 = time.perf_counter()
         oracle.prune_streams(kh, ph, wl["t"], wl["qc"], wl["qn"], wl["rb"], cfg.budget, cfg.n_kv_heads,
-                             stream_ids=ids, form="fac", n_threads=threads, pre_rope=pre_rope)
+                             stream_ids=ids, form=form, n_threads=threads, pre_rope=pre_rope, weight_r=weight_r)
         return time.perf_counter() - t0
 
     n = max(1, min(threads, kk.shape[0]))
@@ -423,7 +427,7 @@ def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False):
             dt = run(np.arange(n))
     keys = n * N
     return {"value": round(keys / dt, 1), "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {kk.shape[0]} streams ({keys} keys), fp64 factored form, {dt:.1f} s",
+            "sample": f"{n} of {kk.shape[0]} streams ({keys} keys), fp64 {form} form, {dt:.1f} s",
             "cpu": cpu_model(), "gpu_over_cpu": round(gpu_keys_s / (keys / dt), 1)}
 
 

@@ -65,6 +65,11 @@ typedef enum { TRIA_BF16 = 0, TRIA_F32 = 1 } tria_dtype;
                                  mix of zhichai.net section "TriAttention：把理论变成算法" item 3,
                                  per band (the norm term keeps its (1 - R_f) weight).  Not
                                  combined with the two flags above (TRIA_E_UNSUPPORTED). */
+#define TRIA_OFFSET_MAX 8u    /* the trigonometric score is the largest of the per-offset series
+                                 instead of their mean (chenxutan.com/d/2624 section 3.3), plus the
+                                 norm score; |D| matrix-core contractions per key.  bf16 caches and
+                                 at most 32 offsets; combines with TRIA_TRIG_WEIGHT_R, not with the
+                                 per-key flags (TRIA_E_UNSUPPORTED). */
 
 typedef struct tria_calib tria_calib; /* opaque, library-owned, immutable after load */
 

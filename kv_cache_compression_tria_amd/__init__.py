@@ -23,6 +23,7 @@ BF16, F32 = 0, 1
 PER_KEY_PHASE = 1
 KEYS_PRE_ROPE = 2
 TRIG_WEIGHT_R = 4
+OFFSET_MAX = 8
 
 EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",

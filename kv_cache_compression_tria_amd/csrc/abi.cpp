@@ -96,12 +96,14 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     std::vector<float2> P32(nh * TRIA_HALF);
     std::vector<float> W(nh * TRIA_HALF);
     std::vector<float> PW(nh * TRIA_HALF * 3);   // [L][Hkv][64][3][G]: Re P, Im P, W of the group
+    std::vector<double2> Qc(nh * TRIA_HALF);     // qbar_f as complex numbers
     for (size_t hh = 0; hh < nh; ++hh) {
         for (int f = 0; f < TRIA_HALF; ++f) {
             const double qr = qc[hh * TRIA_D + f], qi = qc[hh * TRIA_D + TRIA_HALF + f];
             const double pr = qr * C[f] - qi * S[f];
             const double pi = qr * S[f] + qi * C[f];
             P[hh * TRIA_HALF + f] = make_double2(pr, pi);
+            Qc[hh * TRIA_HALF + f] = make_double2(qr, qi);
             P32[hh * TRIA_HALF + f] = make_float2((float)pr, (float)pi);
             W[hh * TRIA_HALF + f] = (float)((1.0 - (double)rb[hh * TRIA_HALF + f]) * (double)qn[hh * TRIA_HALF + f]);
             const size_t grp = hh / G, h = hh % G;
@@ -123,7 +125,9 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     const size_t bnu = tria::align256(sizeof(uint64_t) * TRIA_HALF);
     const size_t bPW = tria::align256(sizeof(float) * PW.size());
     const size_t bR = tria::align256(sizeof(float) * nh * TRIA_HALF);
-    c->block_bytes = bP + bP32 + bW + bnu + bPW + bR;
+    const size_t bQc = tria::align256(sizeof(double2) * nh * TRIA_HALF);
+    const size_t bOff = tria::align256(sizeof(int64_t) * off.size());
+    c->block_bytes = bP + bP32 + bW + bnu + bPW + bR + bQc + bOff;
     if (hipMalloc(&c->block, c->block_bytes) != hipSuccess) { delete c; return TRIA_E_NOMEM; }
     char *b = (char *)c->block;
     c->P = (double2 *)b;
@@ -132,6 +136,8 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     c->nu = (uint64_t *)(b + bP + bP32 + bW);
     c->PW = (float *)(b + bP + bP32 + bW + bnu);
     c->R = (float *)(b + bP + bP32 + bW + bnu + bPW);
+    c->Qc = (double2 *)(b + bP + bP32 + bW + bnu + bPW + bR);
+    c->off = (int64_t *)(b + bP + bP32 + bW + bnu + bPW + bR + bQc);
     hipStream_t st = (hipStream_t)stream;
     bool ok = hipStreamSynchronize(st) == hipSuccess;
     ok = ok && hipMemcpy(c->P, P.data(), sizeof(double2) * P.size(), hipMemcpyHostToDevice) == hipSuccess;
@@ -140,6 +146,8 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
     ok = ok && hipMemcpy(c->nu, nu.data(), sizeof(uint64_t) * TRIA_HALF, hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->PW, PW.data(), sizeof(float) * PW.size(), hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipMemcpy(c->R, rb, sizeof(float) * nh * TRIA_HALF, hipMemcpyHostToDevice) == hipSuccess;
+    ok = ok && hipMemcpy(c->Qc, Qc.data(), sizeof(double2) * Qc.size(), hipMemcpyHostToDevice) == hipSuccess;
+    ok = ok && hipMemcpy(c->off, off.data(), sizeof(int64_t) * off.size(), hipMemcpyHostToDevice) == hipSuccess;
     if (!ok) {
         (void)hipFree(c->block);
         delete c;
@@ -182,8 +190,11 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     if (!c || !k || !t || !F) return TRIA_E_INVALID;
     if (dt != TRIA_BF16 && dt != TRIA_F32) return TRIA_E_INVALID;
     if (n_seq <= 0 || N <= 0 || N > (1 << 24)) return TRIA_E_INVALID;
-    if ((flags & ~(TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE | TRIA_TRIG_WEIGHT_R)) != 0) return TRIA_E_INVALID;
-    if ((flags & TRIA_TRIG_WEIGHT_R) && (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE))) return TRIA_E_UNSUPPORTED;
+    if ((flags & ~(TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE | TRIA_TRIG_WEIGHT_R | TRIA_OFFSET_MAX)) != 0)
+        return TRIA_E_INVALID;
+    if ((flags & (TRIA_TRIG_WEIGHT_R | TRIA_OFFSET_MAX)) && (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)))
+        return TRIA_E_UNSUPPORTED;
+    if ((flags & TRIA_OFFSET_MAX) && (dt != TRIA_BF16 || c->n_off > tria::kMaxdOffsetsLimit)) return TRIA_E_UNSUPPORTED;
     if ((flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) && !pos) return TRIA_E_INVALID;
     if ((size_t)n_seq * c->L * c->Hkv > (size_t)0x7fffffff) return TRIA_E_INVALID;
     if (!aligned(k, 16) || !aligned(F, 4) || (raw && !aligned(raw, 4)) || (stats && !aligned(stats, 4)) ||

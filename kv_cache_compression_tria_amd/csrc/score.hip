@@ -502,6 +502,8 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
 {
     if (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE))
         return launch_score_perkey(c, dt, k, pos, t, n_seq, N, flags, F, raw, stats, lay, ws, st);
+    if (flags & TRIA_OFFSET_MAX)
+        return launch_score_maxd(c, k, t, n_seq, N, qrot, (flags & TRIA_TRIG_WEIGHT_R) != 0, F, raw, stats, lay, ws, st);
     // bf16 caches score on the matrix cores; fp32 caches on the vector ALU
     return dt == TRIA_BF16 ? launch_score_mfma(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st)
                            : launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);

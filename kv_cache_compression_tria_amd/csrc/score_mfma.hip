@@ -832,15 +832,211 @@ static hipError_t launch_cluster_g(const ClusterPlan &pl, const u32x4 *kp, const
                                       args, (unsigned)lds, st);
 }
 
+// ---- maximum over the future offsets (TRIA_OFFSET_MAX) ------------------------------------------
+// The trigonometric score as the largest of the per-offset series (chenxutan.com/d/2624 section
+// 3.3): S_trig(j) = max_{d in D} sum_f Re[qbar_f e^{i w_f (t + d)} conj(ktilde_{j,f})], plus the
+// unchanged norm score.  Per offset the series is a dot product of the key with a query rotated to
+// t + d, so each offset is one more matrix-core contraction: |D| x 4 MFMAs per 16-key tile, whose
+// A operands (the rotated queries, two bf16 terms each) a block builds once in LDS from qbar (fp64,
+// exact turn fractions, optionally scaled by R_f) and reads back per tile.  The norm part uses the
+// regular operands.  One block of 4 waves per (stream, kMaxdKeys-key chunk); raw scores go
+// head-major to the workspace, per-chunk sums around 0 to the partials, and the statistics and
+// z-max kernels of the tiled path finish.
+constexpr int kMaxdKeys = 8192;
+constexpr int kMaxdOffsets = kMaxdOffsetsLimit;   // offsets whose operands fit the block's LDS (4 KB each)
+
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_maxd_kernel(
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const double2 *__restrict__ Qc,
+    const float *__restrict__ R, const uint64_t *__restrict__ nu, const int64_t *__restrict__ off, int n_off,
+    const int32_t *__restrict__ t, int L, int Hkv, int N, int chunks, float *__restrict__ raw,
+    double *__restrict__ part)
+{
+    extern __shared__ u32x4 opsd[];                // [n_off][4 K-blocks][64 lanes]
+    __shared__ BlockSums bs;
+    const int sid = blockIdx.x / chunks;
+    const int chunk = blockIdx.x - sid * chunks;
+    const int g = sid % Hkv;
+    const int l = (sid / Hkv) % L;
+    const int s = sid / (Hkv * L);
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jj = lane & 15, ha = head_a(lane >> 4);
+
+    // ---- per-offset operands in LDS: zero (rows of heads >= G), then scatter the terms
+    for (int i = threadIdx.x; i < n_off * 4 * 64; i += kScoreThreads) opsd[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    {
+        __bf16 *ob = (__bf16 *)opsd;
+        const int64_t ts = t[s];
+        const size_t hh0 = ((size_t)l * Hkv + g) * G;
+        for (int i = threadIdx.x; i < n_off * G * TRIA_HALF; i += kScoreThreads) {
+            const int d = i / (G * TRIA_HALF);
+            const int r = i - d * (G * TRIA_HALF);
+            const int h = r / TRIA_HALF, f = r - h * TRIA_HALF;
+            const uint64_t turns = (uint64_t)(ts + off[d]) * nu[f];     // (t + d) w_f / 2pi mod 1, exact
+            double sn, cs;
+            sincospi(2.0 * ((double)(int64_t)turns * 0x1p-64), &sn, &cs);
+            const double2 q = Qc[(hh0 + h) * TRIA_HALF + f];
+            const double wr = R ? (double)R[(hh0 + h) * TRIA_HALF + f] : 1.0;
+            const float comp[2] = {(float)(wr * (q.x * cs - q.y * sn)), (float)(wr * (q.x * sn + q.y * cs))};
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int dim = f + c * TRIA_HALF;          // real part at f, imaginary at f + 64
+                const int kb = dim >> 5, grp = (dim >> 3) & 3, e = dim & 7;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int ln = grp * 16 + 8 * b + h;    // A row 8b + h, K chunk grp
+                    ob[(((size_t)d * 4 + kb) * 64 + ln) * 8 + e] = (__bf16)bf16_term(comp[c], b);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    Ops c;
+    load_ops(c, ops + (size_t)sid * kOps * 64);
+    Sums m[2];
+    m[0].init();
+    m[1].init();
+    const int j0 = chunk * kMaxdKeys;
+    const int nkeys = min(kMaxdKeys, N - j0);
+    const int ntiles16 = (nkeys + 15) >> 4;
+    const u32x4 *kb = k + ((size_t)sid * N + j0) * 16;
+    const int nt_w = wid < ntiles16 ? (ntiles16 - wid + 3) >> 2 : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        raw + (size_t)sid * G * N + j0, 0, ((G - 1) * N + nkeys) * 4, 0x00020000);
+    constexpr int kDrop = 0x7fffffff;
+    auto issue = [&](u32x4 (&bt)[4], int i) {
+        const int tt = min(wid + 4 * i, ntiles16 - 1);
+        load_tile(bt, kb + (size_t)tt * 16 * 16, nkeys - tt * 16);
+    };
+    auto compute = [&](const u32x4 (&ka)[4], int i) {
+        const int tt = wid + 4 * i;
+        // norm part: band norms as in score_tile16, against the regular norm operands
+        floatx4 accn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const u32x4 x = ka[half], y = ka[2 + half];
+            u32x4 t0, t1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t p0 = __builtin_amdgcn_perm(y[q], x[q], 0x05040100u);
+                const uint32_t p1 = __builtin_amdgcn_perm(y[q], x[q], 0x07060302u);
+                const float n0 = __builtin_amdgcn_sqrtf(band_sq(p0));
+                const float n1 = __builtin_amdgcn_sqrtf(band_sq(p1));
+                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{n0, n1}, bf16x2));
+                const float r0 = n0 - __builtin_bit_cast(float, hi << 16);
+                const float r1 = n1 - __builtin_bit_cast(float, hi & 0xffff0000u);
+                t0[q] = hi;
+                t1[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r0, r1}, bf16x2));
+            }
+            accn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[0][half], __builtin_bit_cast(bf16x8, t0), accn, 0, 0, 0);
+            accn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[1][half], __builtin_bit_cast(bf16x8, t1), accn, 0, 0, 0);
+        }
+        // trigonometric part: the largest per-offset series
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+        for (int d = 0; d < n_off; ++d) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, opsd[(d * 4 + q) * 64 + lane]),
+                                                              __builtin_bit_cast(bf16x8, ka[q]), acc, 0, 0, 0);
+            float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+            permlane32_swap(a0, a1);
+            permlane32_swap(a2, a3);
+            mx0 = fmaxf(mx0, a0 + a1);
+            mx1 = fmaxf(mx1, a2 + a3);
+        }
+        float n0 = accn[0], n1 = accn[1], n2 = accn[2], n3 = accn[3];
+        permlane32_swap(n0, n1);
+        permlane32_swap(n2, n3);
+        const float v0 = mx0 + (n0 + n1), v1 = mx1 + (n2 + n3);
+        const int key = tt * 16 + jj;
+        const bool in = key < nkeys;
+        if (in && ha < G) m[0].add(v0, 0.f);
+        if (in && ha + 2 < G) m[1].add(v1, 0.f);
+        const int o0 = (in && ha < G) ? (ha * N + key) * 4 : kDrop;
+        const int o1 = (in && ha + 2 < G) ? ((ha + 2) * N + key) * 4 : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v0), rsrc, o0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), rsrc, o1, 0, 0);
+    };
+    if (nt_w > 0) TRIA_RING4(nt_w, issue, compute);
+    block_sums_stage(bs, m);
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        const Sums t2 = block_sums_of(bs, h);
+        double *q = part + (((size_t)sid * chunks + chunk) * G + h) * 4;
+        q[0] = t2.s1;
+        q[1] = t2.s2;
+        q[2] = (double)t2.mn;
+        q[3] = (double)t2.mx;
+    }
+}
+
+template <int G>
+static hipError_t launch_maxd_g(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N,
+                                const float *qrot, bool weight_r, float *F, float *raw_out, float *stats,
+                                const tria_score_ws &lay, char *ws, hipStream_t st)
+{
+    const int streams = n_seq * c->L * c->Hkv;
+    const u32x4 *kp = (const u32x4 *)k;
+    u32x4 *ops = (u32x4 *)(ws + lay.ops_off);
+    float *pivot = (float *)(ws + lay.pivot_off);
+    prep_operands_kernel<G><<<streams, 64, 0, st>>>(kp, qrot, c->W, c->L, c->Hkv, N, ops, pivot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    static bool attr_set = false;
+    if (!attr_set) {
+        e = hipFuncSetAttribute((const void *)score_maxd_kernel<G>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMaxdOffsets * 4 * 64 * 16);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
+    double *part = (double *)(ws + lay.part_off);
+    const int chunks = (N + kMaxdKeys - 1) / kMaxdKeys;
+    const long long blocks = (long long)streams * chunks;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    {
+        KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
+        score_maxd_kernel<G><<<(unsigned)blocks, kScoreThreads, (size_t)c->n_off * 4 * 64 * 16, st>>>(
+            kp, ops, c->Qc, weight_r ? c->R : nullptr, c->nu, c->off, c->n_off, t, c->L, c->Hkv, N, chunks, raw, part);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    return launch_tile_finish(G, streams, N, chunks, raw, part, nullptr, F, stats, lay, ws, st);
+}
+
+hipError_t launch_score_maxd(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, const float *qrot,
+                             bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws,
+                             hipStream_t st)
+{
+    if (c->n_off > kMaxdOffsets) return hipErrorInvalidValue;
+    switch (c->G) {
+    case 1: return launch_maxd_g<1>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 2: return launch_maxd_g<2>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 3: return launch_maxd_g<3>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 4: return launch_maxd_g<4>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 5: return launch_maxd_g<5>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 6: return launch_maxd_g<6>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 7: return launch_maxd_g<7>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 8: return launch_maxd_g<8>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 // ---- launch ------------------------------------------------------------------------------------
 template <int G>
-static hipError_t launch_tile_finish_g(int streams, int N, const float *raw, const double *part, const float *pivot,
-                                       float *F, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+static hipError_t launch_tile_finish_g(int streams, int N, int tiles, const float *raw, const double *part,
+                                       const float *pivot, float *F, float *stats, const tria_score_ws &lay, char *ws,
+                                       hipStream_t st)
 {
     KernelTimer timer(TRIA_TIMER_NORMALISE, st);
     int *err = (int *)(ws + lay.err_off);
     float *zst = (float *)(ws + lay.zst_off);
-    tile_stats_kernel<G><<<streams, kScoreThreads, 0, st>>>(part, pivot, N, lay.tiles, zst, stats, err);
+    tile_stats_kernel<G><<<streams, kScoreThreads, 0, st>>>(part, pivot, N, tiles, zst, stats, err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long blocks = (long long)streams * ((N + kZmaxKeys - 1) / kZmaxKeys);
@@ -849,18 +1045,19 @@ static hipError_t launch_tile_finish_g(int streams, int N, const float *raw, con
     return hipGetLastError();
 }
 
-hipError_t launch_tile_finish(int G, int streams, int N, const float *raw, const double *part, const float *pivot,
-                              float *F, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+hipError_t launch_tile_finish(int G, int streams, int N, int tiles, const float *raw, const double *part,
+                              const float *pivot, float *F, float *stats, const tria_score_ws &lay, char *ws,
+                              hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_tile_finish_g<1>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 2: return launch_tile_finish_g<2>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 3: return launch_tile_finish_g<3>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 4: return launch_tile_finish_g<4>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 5: return launch_tile_finish_g<5>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 6: return launch_tile_finish_g<6>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 7: return launch_tile_finish_g<7>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
-    case 8: return launch_tile_finish_g<8>(streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    case 1: return launch_tile_finish_g<1>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 2: return launch_tile_finish_g<2>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 3: return launch_tile_finish_g<3>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 4: return launch_tile_finish_g<4>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 5: return launch_tile_finish_g<5>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 6: return launch_tile_finish_g<6>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 7: return launch_tile_finish_g<7>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
+    case 8: return launch_tile_finish_g<8>(streams, N, tiles, raw, part, pivot, F, stats, lay, ws, st);
     }
     return hipErrorInvalidValue;
 }
@@ -904,7 +1101,7 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    return launch_tile_finish(G, streams, N, raw, part, pivot, F, stats, lay, ws, st);
+    return launch_tile_finish(G, streams, N, lay.tiles, raw, part, pivot, F, stats, lay, ws, st);
 }
 
 hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,

@@ -225,7 +225,7 @@ hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k
     }
     if (e != hipSuccess) return e;
     // statistics around 0 (no pivot) and the z-max of the matrix-core tiled path
-    return launch_tile_finish(c->G, n_seq * c->L * c->Hkv, N, raw, part, nullptr, F, stats, lay, ws, st);
+    return launch_tile_finish(c->G, n_seq * c->L * c->Hkv, N, lay.tiles, raw, part, nullptr, F, stats, lay, ws, st);
 }
 
 }  // namespace tria

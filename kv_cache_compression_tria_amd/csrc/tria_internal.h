@@ -27,6 +27,8 @@ struct tria_calib {
     uint64_t *nu;    // [64] w_f / (2 pi) as a 64-bit fraction of a turn
     float *PW;       // [L][Hkv][64][3][G] Re P32, Im P32 and W of each KV group, band-major
     float *R;        // [L][Hq][64] R_f (the weight of the trigonometric term under TRIA_TRIG_WEIGHT_R)
+    double2 *Qc;     // [L][Hq][64] qbar_f itself (fp64 complex), for the per-offset series
+    int64_t *off;    // [n_off] the future offsets D
 };
 
 // Workspace layout of tria_score (every region 256-byte aligned).
@@ -82,8 +84,14 @@ hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int 
                              float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
 // per-head statistics and z-max of the tiled paths over raw [streams][G][N] and the tile partials
 // part [streams][tiles][G][4] (sums around pivot[stream][h], or around 0 when pivot is null)
-hipError_t launch_tile_finish(int G, int streams, int N, const float *raw, const double *part, const float *pivot,
-                              float *F, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+hipError_t launch_tile_finish(int G, int streams, int N, int tiles, const float *raw, const double *part,
+                              const float *pivot, float *F, float *stats, const tria_score_ws &lay, char *ws,
+                              hipStream_t st);
+// TRIA_OFFSET_MAX scoring (matrix cores, bf16 keys): the largest per-offset trigonometric series
+hipError_t launch_score_maxd(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, const float *qrot,
+                             bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws,
+                             hipStream_t st);
+constexpr int kMaxdOffsetsLimit = 32;   // TRIA_OFFSET_MAX: most future offsets supported
 // TRIA_PER_KEY_PHASE / TRIA_KEYS_PRE_ROPE scoring (vector ALU, any dtype)
 hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
                                const int32_t *t, int n_seq, int N, unsigned flags, float *F, float *raw_out,

@@ -140,3 +140,62 @@ def test_weight_r_with_per_key_flags_is_unsupported(T):
             T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=T.TRIG_WEIGHT_R | extra)
         assert e.value.status == T.E_UNSUPPORTED
     calib.free()
+
+
+# ---- maximum over the future offsets (TRIA_OFFSET_MAX) -------------------------------------------
+
+def test_offset_max_config2(orc, T):
+    gc.run_case(orc, T, synth.CONFIGS[2], form="max", flags=T.OFFSET_MAX)
+
+
+@pytest.mark.parametrize("G", [1, 3, 5, 8])
+def test_offset_max_group_sizes(orc, T, G):
+    cfg = gc.variant(2, name=f"omax-g{G}", n_q_heads=2 * G, n_kv_heads=2, n_seq=2, n_keys=700, budget=500,
+                     t_fixed=9000, calib="uniform_r", r_range=(0.6, 0.99), seed=370 + G)
+    gc.run_case(orc, T, cfg, form="max", flags=T.OFFSET_MAX)
+
+
+@pytest.mark.parametrize("G,N", [(8, 5000), (2, 20000)])
+def test_offset_max_chunks_and_ragged_tail(orc, T, G, N):
+    """Several 8192-key chunks per stream (N = 20000) and a ragged last tile."""
+    cfg = gc.variant(2, name=f"omax-g{G}-N{N}", n_q_heads=G, n_kv_heads=1, n_seq=2, n_keys=N, budget=N // 3 + 7,
+                     t_fixed=N + 1000, calib="head_r", r_range=(0.6, 0.99), seed=380 + G)
+    gc.run_case(orc, T, cfg, form="max", flags=T.OFFSET_MAX)
+
+
+def test_offset_max_with_weight_r(orc, T):
+    cfg = gc.variant(2, name="omax-wr", n_q_heads=8, n_kv_heads=2, n_seq=2, n_keys=1500, budget=600,
+                     t_fixed=3000, calib="head_r", r_range=(0.3, 0.99), seed=390)
+    gc.run_case(orc, T, cfg, form="max", flags=T.OFFSET_MAX | T.TRIG_WEIGHT_R)
+
+
+def test_offset_max_custom_offsets(orc, T):
+    """A caller's own offset set (three offsets, one of them 0)."""
+    import torch
+    cfg = gc.variant(2, name="omax-off", n_q_heads=4, n_kv_heads=1, n_seq=1, n_keys=900, budget=300, t_fixed=5000,
+                     seed=391)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    offs = (0, 5, 1000)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1, cfg.theta, offsets=offs)
+    raw = torch.empty((1, 1, 4, 900), dtype=torch.float32, device="cuda")
+    T.score(calib, dev["k"], dev["t_dev"], raw=raw, flags=T.OFFSET_MAX, check=True)
+    torch.cuda.synchronize()
+    res = orc.prune_streams(gc.streams_of(wl["k"], 900), gc.streams_of(wl["pos"], 900), wl["t"], wl["qc"], wl["qn"],
+                            wl["rb"], 300, 1, offsets=offs, form="max", want_raw=True)
+    gc.check_raw(raw.cpu().numpy().reshape(1, 4, 900), res["raw"])
+    calib.free()
+
+
+def test_offset_max_unsupported_cases(T):
+    cfg = gc.variant(1, name="omax-f32", n_keys=256, budget=64, seed=392, positions="contiguous", t_fixed=300)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    with pytest.raises(T.TriaError) as e:                      # fp32 cache
+        T.score(calib, dev["k"], dev["t_dev"], flags=T.OFFSET_MAX)
+    assert e.value.status == T.E_UNSUPPORTED
+    with pytest.raises(T.TriaError) as e:                      # with a per-key flag
+        T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=T.OFFSET_MAX | T.PER_KEY_PHASE)
+    assert e.value.status == T.E_UNSUPPORTED
+    calib.free()
