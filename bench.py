@@ -1,15 +1,15 @@
 """Benchmark of the TriAttention prune step on one MI355X.
 
-One step = tria_score + tria_select_topB + tria_compact over every stream of the workload
-(score every cached key, z-score per query head, GQA max, top-B, in-place compaction of K, V and
-positions).  Default workload: Qwen3-32B shapes, 64 layers x 8 sequences x 8 KV heads
+One step = one tria_prune call (tria_score, tria_select_topB and tria_compact in sequence) over
+every stream of the workload (score every cached key, z-score per query head, GQA max, top-B,
+in-place compaction of K, V and positions); --entry separate makes the three calls itself.  Default workload: Qwen3-32B shapes, 64 layers x 8 sequences x 8 KV heads
 (4096 streams), 32768 bf16 keys per stream compressed to B = 3072.
 
 Before every step, outside the timed region, K, V and positions are restored from a pristine
 device copy and 1 GiB of scratch is written to evict the 256 MB Infinity Cache and the L2, so
 each step reads a cold, unpruned cache.  Each step is timed with HIP events on the stream the
-kernels run on; the per-phase events (score / select / compact) give the dominant kernel's
-duration for the roofline.
+kernels run on; the library's own HIP events around each kernel give the per-kernel times and the
+dominant kernel's duration for the roofline.
 
 Prints one JSON line (see the keys below).  --gpus above 1 is refused: this path runs on one GPU.
 
@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--workload", choices=("prune", "decode", "calib"), default="prune",
                     help="prune: the prune step (default); decode: append 128 tokens + prune per step; "
                          "calib: calibration statistics of captured queries")
+    ap.add_argument("--entry", choices=("prune", "separate"), default="prune",
+                    help="prune: one tria_prune call per step (default); separate: tria_score, "
+                         "tria_select_topB and tria_compact")
     ap.add_argument("--score-path", choices=("auto", "tiled"), default="auto",
                     help="long-stream bf16 scoring: auto (stream clusters keep raw scores on chip) or tiled")
     ap.add_argument("--variant", choices=VARIANTS, default="default",
@@ -161,11 +164,18 @@ def main():
 
     def step():
         ev[0].record(stream)
-        T.score(calib, k, t, F=F, ws=ws, stream=stream, pos=pos if flags & 3 else None, flags=flags)
-        ev[1].record(stream)
-        T.select_topB(F, B, kept=kept, stream=stream)
-        ev[2].record(stream)
-        T.compact(k, v, pos, kept, B, stream=stream)
+        if args.entry == "prune":
+            # the whole step through its own entry point (selection and compaction fused when
+            # the shapes allow)
+            T.prune(calib, k, v, pos, t, B, F=F, kept=kept, flags=flags, ws=ws, stream=stream)
+            ev[1].record(stream)
+            ev[2].record(stream)
+        else:
+            T.score(calib, k, t, F=F, ws=ws, stream=stream, pos=pos if flags & 3 else None, flags=flags)
+            ev[1].record(stream)
+            T.select_topB(F, B, kept=kept, stream=stream)
+            ev[2].record(stream)
+            T.compact(k, v, pos, kept, B, stream=stream)
         ev[3].record(stream)
 
     for _ in range(args.warmup):
@@ -233,13 +243,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "streams": n_streams, "keys_per_stream": N, "budget": B,
                    "layers": L, "seqs": S, "q_heads": cfg.n_q_heads, "kv_heads": Hkv, "head_dim": d,
-                   "cache_dtype": cfg.dtype, "score_variant": args.variant, "score_path": args.score_path, "parallelism": "single-gpu"},
+                   "cache_dtype": cfg.dtype, "score_variant": args.variant, "score_path": args.score_path,
+                   "entry": "tria_prune" if args.entry == "prune" else "tria_score+tria_select_topB+tria_compact", "parallelism": "single-gpu"},
         "alg_bytes_per_step": int(alg),
         "alg_GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "moved_rows": moved,
-        "phases_ms": {"score": round(float(ph[0]), 4), "select": round(float(ph[1]), 4),
-                      "compact": round(float(ph[2]), 4)},
+        "phases_ms": ({"score": round(float(ph[0]), 4), "select": round(float(ph[1]), 4),
+                       "compact": round(float(ph[2]), 4)} if args.entry == "separate" else
+                      {name: kv["avg_ms"] for name, kv in kernels.items()}),
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernels[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic().get(dom)},

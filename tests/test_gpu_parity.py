@@ -229,6 +229,30 @@ def test_prune_entry_point_matches_separate_calls(T):
     assert torch.equal(d1["k"], d2["k"]) and torch.equal(d1["v"], d2["v"]) and torch.equal(d1["pos"], d2["pos"])
 
 
+@pytest.mark.parametrize("dtype,G,N,B", [("bf16", 4, 5000, 1673), ("f32", 2, 3001, 1000), ("bf16", 8, 32768, 3072),
+                                          ("bf16", 4, 9000, 4096), ("bf16", 4, 700, 1), ("bf16", 2, 1025, 1024)])
+def test_prune_matches_separate_calls_shapes(T, dtype, G, N, B):
+    """tria_prune's F, kept indices and compacted K, V, positions equal those of the three
+    separate calls bit for bit, across on-chip, cluster and fp32 shapes and ragged sizes."""
+    import torch
+    print(f"\n[case] prune vs separate {dtype} G={G} N={N} B={B}", flush=True)
+    n_layers = 2 if N > 20000 else 1
+    cfg = variant(2, name=f"prune-{dtype}-N{N}", n_q_heads=2 * G, n_kv_heads=2, n_seq=2, n_layers=n_layers,
+                  n_keys=N, budget=B, dtype=dtype, t_fixed=N + 500, calib="head_r", r_range=(0.6, 0.99),
+                  seed=40 + G)
+    wl = synth.make_host(cfg)
+    d1, d2 = synth.to_device(wl), synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    F1 = T.score(calib, d1["k"], d1["t_dev"], check=True)
+    kept1 = T.select_topB(F1, B)
+    T.compact(d1["k"], d1["v"], d1["pos"], kept1, B)
+    F2, kept2 = T.prune(calib, d2["k"], d2["v"], d2["pos"], d2["t_dev"], B)
+    torch.cuda.synchronize()
+    assert torch.equal(F1, F2) and torch.equal(kept1, kept2)
+    assert torch.equal(d1["k"], d2["k"]) and torch.equal(d1["v"], d2["v"]) and torch.equal(d1["pos"], d2["pos"])
+    calib.free()
+
+
 def test_config3_full_size_sampled_streams(orc, T):
     rng = np.random.default_rng(3)
     sample = np.sort(rng.choice(synth.CONFIGS[3].n_streams, 24, replace=False))
