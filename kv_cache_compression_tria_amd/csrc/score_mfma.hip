@@ -903,17 +903,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_maxd_kernel(
     const int nkeys = min(kMaxdKeys, N - j0);
     const int ntiles16 = (nkeys + 15) >> 4;
     const u32x4 *kb = k + ((size_t)sid * N + j0) * 16;
-    const int nt_w = wid < ntiles16 ? (ntiles16 - wid + 3) >> 2 : 0;
+    // items of a wave: pairs of consecutive 16-key tiles 2p, 2p + 1 for p = wid, wid + 4, ...; each
+    // operand read from LDS serves both tiles
+    const int npairs = (ntiles16 + 1) >> 1;
+    const int nt_w = wid < npairs ? (npairs - wid + 3) >> 2 : 0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         raw + (size_t)sid * G * N + j0, 0, ((G - 1) * N + nkeys) * 4, 0x00020000);
     constexpr int kDrop = 0x7fffffff;
-    auto issue = [&](u32x4 (&bt)[4], int i) {
-        const int tt = min(wid + 4 * i, ntiles16 - 1);
-        load_tile(bt, kb + (size_t)tt * 16 * 16, nkeys - tt * 16);
+    auto issue = [&](u32x4 (&bt)[2][4], int i) {
+        const int pr = min(wid + 4 * i, npairs - 1);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tt = min(2 * pr + q, ntiles16 - 1);
+            load_tile(bt[q], kb + (size_t)tt * 16 * 16, nkeys - tt * 16);
+        }
     };
-    auto compute = [&](const u32x4 (&ka)[4], int i) {
-        const int tt = wid + 4 * i;
-        // norm part: band norms as in score_tile16, against the regular norm operands
+    // band norms of a tile against the regular norm operands (as in score_tile16)
+    auto norm_part = [&](const u32x4 (&ka)[4]) {
         floatx4 accn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -934,34 +940,89 @@ __global__ __launch_bounds__(kScoreThreads) void score_maxd_kernel(
             accn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[0][half], __builtin_bit_cast(bf16x8, t0), accn, 0, 0, 0);
             accn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[1][half], __builtin_bit_cast(bf16x8, t1), accn, 0, 0, 0);
         }
-        // trigonometric part: the largest per-offset series
-        float mx0 = -INFINITY, mx1 = -INFINITY;
-        for (int d = 0; d < n_off; ++d) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, opsd[(d * 4 + q) * 64 + lane]),
-                                                              __builtin_bit_cast(bf16x8, ka[q]), acc, 0, 0, 0);
-            float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
-            permlane32_swap(a0, a1);
-            permlane32_swap(a2, a3);
-            mx0 = fmaxf(mx0, a0 + a1);
-            mx1 = fmaxf(mx1, a2 + a3);
-        }
-        float n0 = accn[0], n1 = accn[1], n2 = accn[2], n3 = accn[3];
-        permlane32_swap(n0, n1);
-        permlane32_swap(n2, n3);
-        const float v0 = mx0 + (n0 + n1), v1 = mx1 + (n2 + n3);
-        const int key = tt * 16 + jj;
-        const bool in = key < nkeys;
-        if (in && ha < G) m[0].add(v0, 0.f);
-        if (in && ha + 2 < G) m[1].add(v1, 0.f);
-        const int o0 = (in && ha < G) ? (ha * N + key) * 4 : kDrop;
-        const int o1 = (in && ha + 2 < G) ? ((ha + 2) * N + key) * 4 : kDrop;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v0), rsrc, o0, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), rsrc, o1, 0, 0);
+        return accn;
     };
-    if (nt_w > 0) TRIA_RING4(nt_w, issue, compute);
+    auto compute = [&](const u32x4 (&bt)[2][4], int i) {
+        const int pr = wid + 4 * i;
+        floatx4 accn[2] = {norm_part(bt[0]), norm_part(bt[1])};
+        // trigonometric part: the largest per-offset series, both tiles per operand read
+        float mx[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+        // two offsets per step (four independent accumulator chains), so that one offset's
+        // products run while the other's operands arrive and results are combined
+        auto fold = [&](floatx4 (&acc)[2]) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float a0 = acc[q][0], a1 = acc[q][1], a2 = acc[q][2], a3 = acc[q][3];
+                permlane32_swap(a0, a1);
+                permlane32_swap(a2, a3);
+                mx[q][0] = fmaxf(mx[q][0], a0 + a1);
+                mx[q][1] = fmaxf(mx[q][1], a2 + a3);
+            }
+        };
+        auto products = [&](int d, floatx4 (&acc)[2]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, opsd[(d * 4 + q) * 64 + lane]);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bt[0][q]), acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bt[1][q]), acc[1], 0, 0, 0);
+            }
+        };
+        int d = 0;
+        for (; d + 1 < n_off; d += 2) {
+            floatx4 acc0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            floatx4 acc1[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            products(d, acc0);
+            products(d + 1, acc1);
+            fold(acc0);
+            fold(acc1);
+        }
+        if (d < n_off) {
+            floatx4 acc0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            products(d, acc0);
+            fold(acc0);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float n0 = accn[q][0], n1 = accn[q][1], n2 = accn[q][2], n3 = accn[q][3];
+            permlane32_swap(n0, n1);
+            permlane32_swap(n2, n3);
+            const float v0 = mx[q][0] + (n0 + n1), v1 = mx[q][1] + (n2 + n3);
+            const int tt = 2 * pr + q;
+            const int key = tt * 16 + jj;
+            const bool in = tt < ntiles16 && key < nkeys;
+            if (in && ha < G) m[0].add(v0, 0.f);
+            if (in && ha + 2 < G) m[1].add(v1, 0.f);
+            const int o0 = (in && ha < G) ? (ha * N + key) * 4 : kDrop;
+            const int o1 = (in && ha + 2 < G) ? ((ha + 2) * N + key) * 4 : kDrop;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v0), rsrc, o0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), rsrc, o1, 0, 0);
+        }
+    };
+    if (nt_w > 0) {
+        u32x4 r0[2][4], r1[2][4], r2[2][4], r3[2][4];
+        const int n4 = (nt_w + 3) & ~3;
+        issue(r0, 0);
+        TRIA_PIN();
+        issue(r1, 1);
+        TRIA_PIN();
+        issue(r2, 2);
+        TRIA_PIN();
+        for (int i = 0; i < n4; i += 4) {
+            issue(r3, i + 3);
+            TRIA_PIN();
+            compute(r0, i);
+            issue(r0, i + 4);
+            TRIA_PIN();
+            compute(r1, i + 1);
+            issue(r1, i + 5);
+            TRIA_PIN();
+            compute(r2, i + 2);
+            issue(r2, i + 6);
+            TRIA_PIN();
+            compute(r3, i + 3);
+            TRIA_PIN();
+        }
+    }
     block_sums_stage(bs, m);
     __syncthreads();
     if (threadIdx.x < G) {
