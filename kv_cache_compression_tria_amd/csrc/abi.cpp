@@ -4,7 +4,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "tria_internal.h"
@@ -29,6 +32,20 @@ uint64_t turn_fraction(double w)
 
 namespace tria {
 std::atomic<int> g_score_path{TRIA_PATH_AUTO};
+
+hipError_t allow_dynamic_lds(const void *kernel, int bytes)
+{
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;   // (kernel, device)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({kernel, dev})) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert({kernel, dev});
+    return e;
+}
 }
 
 extern "C" {

@@ -450,13 +450,8 @@ static hipError_t launch_score_t(const tria_calib *c, const void *k, int n_seq, 
     int *err = (int *)(ws + lay.err_off);
     if (!lay.tiled) {
         const size_t lds = (size_t)G * 192 * 4 + (size_t)G * N * 4;
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)score_fused_kernel<BF16, G>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsMax + G * 192 * 4);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        hipError_t e = allow_dynamic_lds((const void *)score_fused_kernel<BF16, G>, kFusedLdsMax + G * 192 * 4);
+        if (e != hipSuccess) return e;
         KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
         score_fused_kernel<BF16, G><<<streams, kScoreThreads, lds, st>>>(
             (const uint4 *)k, qrot, c->W, c->L, c->Hkv, N, F, raw_out, stats, err);

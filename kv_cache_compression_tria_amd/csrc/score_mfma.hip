@@ -783,13 +783,7 @@ static bool cluster_plan(int N, ClusterPlan &pl)
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
         return false;
     if (!coop || n_cu <= 0) return false;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)score_mfma_cluster_kernel<G, NW>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kClusterLds) != hipSuccess)
-            return false;
-        attr_set = true;
-    }
+    if (allow_dynamic_lds((const void *)score_mfma_cluster_kernel<G, NW>, kClusterLds) != hipSuccess) return false;
     const int kmax = (kClusterLds / (GP * 4)) & ~15;
     int Ps = 1;
     while ((long long)Ps * kmax < N) Ps *= 2;
@@ -1048,13 +1042,8 @@ static hipError_t launch_maxd_g(const tria_calib *c, const void *k, const int32_
     prep_operands_kernel<G><<<streams, 64, 0, st>>>(kp, qrot, c->W, c->L, c->Hkv, N, ops, pivot);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    static bool attr_set = false;
-    if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)score_maxd_kernel<G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMaxdOffsets * 4 * 64 * 16);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    e = allow_dynamic_lds((const void *)score_maxd_kernel<G>, kMaxdOffsets * 4 * 64 * 16);
+    if (e != hipSuccess) return e;
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
     const int chunks = (N + kMaxdKeys - 1) / kMaxdKeys;
@@ -1137,13 +1126,8 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
     if (e != hipSuccess) return e;
     if (!lay.tiled) {
         const size_t lds = (size_t)G * (N | 1) * 4;
-        static bool attr_set = false;
-        if (!attr_set) {
-            e = hipFuncSetAttribute((const void *)score_mfma_fused_kernel<G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kFusedLdsMax);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        e = allow_dynamic_lds((const void *)score_mfma_fused_kernel<G>, kFusedLdsMax);
+        if (e != hipSuccess) return e;
         KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
         score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();

@@ -288,13 +288,8 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
         return hipGetLastError();
     }
     if (N <= kSelectLdsKeys) {
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)select_kernel<true>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kSelectLdsKeys * 4);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        const hipError_t e = allow_dynamic_lds((const void *)select_kernel<true>, kSelectLdsKeys * 4);
+        if (e != hipSuccess) return e;
         select_kernel<true><<<n_streams, kSelectThreads, (size_t)N * 4, st>>>(F, N, B, kept);
     } else {
         select_kernel<false><<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept);

@@ -73,6 +73,10 @@ class KernelTimer {
 
 tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys);
 
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once per (kernel, device);
+// thread-safe.
+hipError_t allow_dynamic_lds(const void *kernel, int bytes);
+
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_rotate(const tria_calib *c, const int32_t *t, int n_seq, float *qrot, int *err, bool weight_r,
                          hipStream_t st);
