@@ -257,3 +257,44 @@ def test_config3_full_size_sampled_streams(orc, T):
     rng = np.random.default_rng(3)
     sample = np.sort(rng.choice(synth.CONFIGS[3].n_streams, 24, replace=False))
     run_case(orc, T, synth.CONFIGS[3], sample=sample)
+
+
+@pytest.mark.parametrize("N,G", [(2176, 4), (9000, 8)])
+def test_prune_step_replays_in_a_hip_graph(T, N, G):
+    """The whole step captured once in a HIP graph (torch.cuda.graph) and replayed several times,
+    with eager work and synchronisations between replays: every replay's F, kept indices and
+    compacted cache equal an eager run's bit for bit (on-chip path N = 2176, stream clusters
+    N = 9000, G = 8)."""
+    import torch
+    print(f"\n[case] graph replay N={N} G={G}", flush=True)
+    cfg = variant(2, name=f"graph-N{N}", n_q_heads=2 * G, n_kv_heads=2, n_seq=2, n_keys=N, budget=N // 4,
+                  t_fixed=N + 100, calib="head_r", r_range=(0.6, 0.99), seed=50 + G)
+    wl = synth.make_host(cfg)
+    ref = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    B = cfg.budget
+    F_ref, kept_ref = T.prune(calib, ref["k"], ref["v"], ref["pos"], ref["t_dev"], B)
+    torch.cuda.synchronize()
+    dev = synth.to_device(wl)
+    k0, v0, p0 = dev["k"].clone(), dev["v"].clone(), dev["pos"].clone()
+    S, L, Hkv = dev["k"].shape[:3]
+    F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device="cuda")
+    kept = torch.empty((S * L * Hkv, B), dtype=torch.int32, device="cuda")
+    ws = T.workspace(T.prune_workspace_bytes(calib, S, N, B, dev["k"].dtype))
+    T.prune(calib, dev["k"], dev["v"], dev["pos"], dev["t_dev"], B, F=F, kept=kept, ws=ws)   # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        T.prune(calib, dev["k"], dev["v"], dev["pos"], dev["t_dev"], B, F=F, kept=kept, ws=ws)
+    for rep in range(3):
+        dev["k"].copy_(k0)
+        dev["v"].copy_(v0)
+        dev["pos"].copy_(p0)
+        F.zero_()
+        kept.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(F, F_ref) and torch.equal(kept, kept_ref), f"replay {rep}"
+        assert torch.equal(dev["k"], ref["k"]) and torch.equal(dev["v"], ref["v"]) and torch.equal(dev["pos"], ref["pos"])
+    calib.free()
