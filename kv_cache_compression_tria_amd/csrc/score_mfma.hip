@@ -318,6 +318,18 @@ struct WaveScorer {
             m[s].init();
         }
     }
+    // the same from an LDS copy of the stream's operand words and pivots
+    __device__ void begin_lds(const u32x4 *ops_l, const float *piv_l)
+    {
+        load_ops(c, ops_l);
+        const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int h = head_a(g) + 2 * s;
+            p[s] = piv_l[h < G ? h : 0];
+            m[s].init();
+        }
+    }
     // score a tile; v[s] = score of key (tile row l%16) for head head_a(g) + 2s.  Rows >= nvalid
     // and heads >= G enter the sums as the pivot itself (no change to the sums; the pivot is the
     // score of key 0, so min and max keep their values): no branches in the key loop.
@@ -583,18 +595,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_fused_kernel(
 // ---- cluster path: the raw scores of a stream stay on chip ----------------------------------
 // A stream too long for one block's LDS is split over a cluster of Ps blocks (Ps a power of two),
 // each keeping the raw scores of its Kb keys in LDS ([Kb][GP] floats, key-major, GP = G rounded up
-// to even).  After scoring, every block publishes its per-head partial sums, waits until the
-// cluster's Ps partials of this round are there, adds them in part order (every block gets the
-// same bits), and writes the final scores of its keys straight from LDS: the raw scores never
-// travel through HBM.  The grid is one block per CU, launched cooperatively so that all blocks
-// are resident at once; a block loops
-// over rounds, cluster c scoring streams c, c + C, c + 2C, ...  The Ps blocks of a cluster sit on
-// one XCD (workgroups are dealt to the 8 XCDs in turn).  The exchanged words are agent-scope
-// atomics, coherent across the device without cache maintenance.  Partial sums are
-// double-buffered by round parity: a block can be at most one round ahead of the slowest block
-// of its cluster.  The wait is bounded: past the bound the block sets bit 2 of the error flag
-// and carries on (wrong scores, but no hang), and every other waiting block then stops at once.
+// to even).  After scoring, every block publishes its per-head partial sums and moves on to the
+// next stream; after the first four items of that stream (scores held in registers) it waits
+// until the cluster's Ps partials of the previous round are there, adds them in part order (every
+// block gets the same bits), and writes the final scores of its keys straight from LDS: the raw
+// scores never travel through HBM, and the wait for the slowest block of the cluster is covered
+// by scoring.  The grid is one block per CU, launched cooperatively so that all blocks are
+// resident at once; a block loops over rounds, cluster c scoring streams c, c + C, c + 2C, ...
+// The Ps blocks of a cluster sit on one XCD (workgroups are dealt to the 8 XCDs in turn).  The
+// exchanged words are agent-scope atomics, coherent across the device without cache
+// maintenance.  Partial sums are double-buffered by round parity: a block publishes round r + 2
+// only after the whole cluster has published round r + 1, and every block has gathered round r
+// before it publishes round r + 1.  The wait is bounded: past the bound the block sets bit 2 of
+// the error flag and carries on (wrong scores, but no hang), and every other waiting block then
+// stops at once.
 constexpr int kClusterWaves = 8;
+constexpr int kClusterDefer = 4;            // groups of four items scored before a round is finished
 constexpr unsigned kSpinLimit = 1u << 20;   // polls of about a microsecond each
 
 template <int G, int NW>
@@ -608,6 +624,9 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
     __shared__ BlockSumsT<NW> bs;
     __shared__ float zmu[8], zinv[8];
     __shared__ double xs[32 * 8 * 4];              // the cluster's partials of a round, gathered
+    __shared__ u32x4 ops_l[kOps * 64];             // the next stream's operand words ...
+    __shared__ float piv_l[8];                     // ... and pivots, fetched during a round
+    static_assert(NW == kOps, "one operand word per thread");
     const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
     const int cl = x * cpx + y / Ps, part = y % Ps;
     const int rounds = cl < streams ? (streams - cl + C - 1) / C : 0;
@@ -620,8 +639,7 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
     const int ntiles16 = (nkeys + 15) >> 4;
     // Every wave takes the same number of items per round, a multiple of four (empty items re-read
     // a real tile and score nothing), so that the four-deep ring runs on across rounds: the loads
-    // of the next round's first tiles are in flight while a round ends (exchange, statistics,
-    // final scores).
+    // of the next round's first tiles are in flight while a round ends (statistics, publication).
     const int nt = (max(1, (ntiles16 + NW - 1) / NW) + 3) & ~3;
     const int total = rounds * nt;
 
@@ -637,63 +655,44 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
         else
             load_tile(b, k + (size_t)sid * N * 16, 0);   // a part with no keys: row 0, scored as empty
     };
-    auto compute = [&](const u32x4 (&b)[4], int li) {
-        const int t = wid + NW * li;
-        float v[2];
-        ws.score(b, nkeys - t * 16, v);
-        const int key = t * 16 + jj;
+    // raw scores of item li of this wave into LDS
+    auto put = [&](int li, const float (&v)[2]) {
+        const int key = (wid + NW * li) * 16 + jj;
         if (key < nkeys) {
             if (ha < GP) lraw[key * GP + ha] = v[0];
             if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
         }
     };
-    u32x4 b0[4], b1[4], b2[4], b3[4];
-    issue(b0, 0);
-    TRIA_PIN();
-    issue(b1, 1);
-    TRIA_PIN();
-    issue(b2, 2);
-    TRIA_PIN();
-    for (int r = 0; r < rounds; ++r) {
-        for (int li = 0; li < nt; li += 4) {
-            const int i = r * nt + li;
-            issue(b3, i + 3);
-            TRIA_PIN();
-            compute(b0, li);
-            issue(b0, i + 4);
-            TRIA_PIN();
-            compute(b1, li + 1);
-            issue(b1, i + 5);
-            TRIA_PIN();
-            compute(b2, li + 2);
-            issue(b2, i + 6);
-            TRIA_PIN();
-            compute(b3, li + 3);
-            TRIA_PIN();
+    auto compute = [&](const u32x4 (&b)[4], int li) {
+        float v[2];
+        ws.score(b, nkeys - (wid + NW * li) * 16, v);
+        put(li, v);
+    };
+    // round r's partial sums: wave 0 of every block stores its per-head sums as agent-scope atomics
+    // (coherent across the device without cache maintenance), waits for the stores, and counts its
+    // arrival.  Nothing waits for the other blocks here.
+    auto publish = [&](int r) {
+        if (wid != 0) return;
+        double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
+        if (lane < G) {
+            const Sums t2 = block_sums_of(bs, lane);
+            double *q = xr + ((size_t)part * G + lane) * 4;
+            __hip_atomic_store(q + 0, t2.s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 1, t2.s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 2, (double)t2.mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 3, (double)t2.mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-
-        // ---- end of round r: exchange partial sums within the cluster, then final scores
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(&arrive[cl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // round r's final scores: wave 0 waits (bounded) until the whole cluster has published round
+    // r, fetches the Ps partials at once and lanes h < G add head h's in part order (every block
+    // gets the same bits); then the block writes F for its keys straight from LDS.
+    auto finish = [&](int r) {
         const int sid = cl + r * C;
-        block_sums_stage(bs, ws.m);
-        __syncthreads();
         if (wid == 0) {
-            // Wave 0 runs the exchange.  The exchanged words are agent-scope atomics (coherent
-            // across the device without cache maintenance): lanes h < G store this block's
-            // partials of head h, the stores are waited for, and only then is the arrival
-            // counted; after lane 0 has seen the whole cluster arrive, the lanes fetch every
-            // partial at once, and lanes h < G add head h's in part order.
-            double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
-            if (lane < G) {
-                const Sums t2 = block_sums_of(bs, lane);
-                double *q = xr + ((size_t)part * G + lane) * 4;
-                __hip_atomic_store(q + 0, t2.s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(q + 1, t2.s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(q + 2, (double)t2.mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(q + 3, (double)t2.mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
             if (lane == 0) {
-                __hip_atomic_fetch_add(&arrive[cl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const uint32_t target = (uint32_t)(r + 1) * (uint32_t)Ps;
                 unsigned spins = 0;
                 while (__hip_atomic_load(&arrive[cl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -709,9 +708,10 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
             __builtin_amdgcn_wave_barrier();
             asm volatile("" ::: "memory");
             for (int q = lane; q < Ps * G; q += 64) {
-                double *src = xr + (size_t)q * 4;
+                const double *src = xr + (size_t)q * 4;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) xs[q * 4 + c] = __hip_atomic_load(src + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int c = 0; c < 4; ++c)
+                    xs[q * 4 + c] = __hip_atomic_load(src + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_wave_barrier();
@@ -751,9 +751,86 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
                 const int h = q / nkeys, j = q - h * nkeys;
                 raw_out[((size_t)sid * G + h) * N + j0 + j] = lraw[j * GP + h];
             }
-        if (r + 1 < rounds) ws.begin(ops, pivot, sid + C);
-        __syncthreads();                           // LDS raw, sums and zmu are reused next round
+        __syncthreads();                           // LDS raw and zmu are reused
+    };
+    u32x4 b0[4], b1[4], b2[4], b3[4];
+    issue(b0, 0);
+    TRIA_PIN();
+    issue(b1, 1);
+    TRIA_PIN();
+    issue(b2, 2);
+    TRIA_PIN();
+    for (int r = 0; r < rounds; ++r) {
+        int li = 0;
+        if (r > 0) {
+            // The first items of a round keep their scores in registers while the previous round
+            // is finished: by then every block of the cluster has long published it, so the wait
+            // for the slowest block is covered by scoring instead of idling.
+            constexpr int D = 4 * kClusterDefer;
+            const int nd = min(D, nt);
+            float dv[D][2];
+#pragma unroll
+            for (int q0 = 0; q0 < D; q0 += 4) {
+                if (q0 < nd) {
+                    const int i = r * nt + q0;
+                    issue(b3, i + 3);
+                    TRIA_PIN();
+                    ws.score(b0, nkeys - (wid + NW * q0) * 16, dv[q0]);
+                    issue(b0, i + 4);
+                    TRIA_PIN();
+                    ws.score(b1, nkeys - (wid + NW * (q0 + 1)) * 16, dv[q0 + 1]);
+                    issue(b1, i + 5);
+                    TRIA_PIN();
+                    ws.score(b2, nkeys - (wid + NW * (q0 + 2)) * 16, dv[q0 + 2]);
+                    issue(b2, i + 6);
+                    TRIA_PIN();
+                    ws.score(b3, nkeys - (wid + NW * (q0 + 3)) * 16, dv[q0 + 3]);
+                    TRIA_PIN();
+                }
+            }
+            finish(r - 1);
+#pragma unroll
+            for (int q = 0; q < D; ++q)
+                if (q < nd) put(q, dv[q]);
+            li = nd;
+        }
+        // the next stream's operands and pivots: fetched now, into LDS at the end of the round
+        const bool more = r + 1 < rounds;
+        u32x4 nxt_op = {0u, 0u, 0u, 0u};
+        float nxt_pv = 0.f;
+        if (more) {
+            const int sn = cl + (r + 1) * C;
+            nxt_op = ops[(size_t)sn * kOps * 64 + threadIdx.x];
+            if (threadIdx.x < G) nxt_pv = pivot[(size_t)sn * G + threadIdx.x];
+        }
+        TRIA_PIN();
+        for (; li < nt; li += 4) {
+            const int i = r * nt + li;
+            issue(b3, i + 3);
+            TRIA_PIN();
+            compute(b0, li);
+            issue(b0, i + 4);
+            TRIA_PIN();
+            compute(b1, li + 1);
+            issue(b1, i + 5);
+            TRIA_PIN();
+            compute(b2, li + 2);
+            issue(b2, i + 6);
+            TRIA_PIN();
+            compute(b3, li + 3);
+            TRIA_PIN();
+        }
+        // ---- end of round r: stage and publish the partial sums, switch to the next stream
+        block_sums_stage(bs, ws.m);
+        if (more) {
+            ops_l[threadIdx.x] = nxt_op;
+            if (threadIdx.x < G) piv_l[threadIdx.x] = nxt_pv;
+        }
+        __syncthreads();
+        publish(r);
+        if (more) ws.begin_lds(ops_l, piv_l);
     }
+    finish(rounds - 1);
 }
 
 __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int n, uint32_t v)
