@@ -2,20 +2,20 @@
 //
 // Keep the B keys with the largest final score, ties to the lower index, written in ascending
 // index order (chenxutan.com/d/2624 section 4.2: top-k of the scores, then sorted to keep the
-// cache order).  One workgroup of 16 waves per stream:
-//   1. map each score to an order-preserving unsigned key (-0 folded onto +0), kept in LDS;
-//   2. three radix digits (11, 11 and 10 bits) find the B-th largest key T and how many of the
-//      keys equal to T must be taken (k): a histogram of digit 0 over all keys picks a bin, the
-//      keys of that bin are copied to a candidate list, and digits 1 and 2 are resolved over the
-//      candidates only.  Final scores cluster in a few exponent values, so the top digit piles
-//      onto few bins: each wave first counts its heavy bins with one ballot per bin and a single
-//      atomic, and only the scattered rest use per-lane atomics;
-//   3. wave w owns the contiguous key range [w*N/16, (w+1)*N/16): it counts its keys > T and
-//      == T, a prefix over the 16 wave totals gives its output base, and it writes every index
-//      with key > T and the first k indices with key == T (in index order) at
-//      slot = #(key > T before j) + min(#(key == T before j), k).
-//   The candidate list of step 2 is written the same way (count, prefix, write): no atomics,
-//   and the candidates keep index order.
+// cache order).  One workgroup of 16 waves per stream.  Scores are mapped to order-preserving
+// unsigned keys (-0 folded onto +0); three radix digits (11, 11 and 10 bits) find the B-th
+// largest key T and how many of the keys equal to T are kept (k): a histogram of digit 0 over all
+// keys picks a bin, the keys of that bin are copied to a candidate list, and digits 1 and 2 are
+// resolved over the candidates alone.  Final scores cluster in a few exponent values, so the top
+// digit piles onto few bins: each wave first counts its heavy bins with one ballot per bin and a
+// single atomic, and only the scattered rest use per-lane atomics.  Every key > T is kept and the
+// first k keys == T (in index order), at slot #(key > T before j) + min(#(key == T before j), k).
+//   select_lds_kernel (streams whose keys fit in LDS): the keys live in LDS; the candidates are
+//     listed in any order; the kept set is written as two bitmaps (> T, == T), and a prefix of the
+//     words' population counts places every kept index.
+//   select_global_kernel (longer streams): the keys are re-read from F in every pass; wave w owns
+//     the contiguous key range [w*N/16, (w+1)*N/16), and the candidate list and the output are
+//     written in index order from per-wave counts and a prefix over the 16 wave totals.
 #include "common.cuh"
 #include "tria_internal.h"
 
@@ -49,6 +49,7 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin, bool live
 constexpr int kBins0 = 2048;      // digit 0: the top 11 bits of the order key
 constexpr int kCand = 4096;       // candidate list (keys of the chosen digit-0 bin), in LDS
 static_assert(kSelectLdsKeys * 4 + (kBins0 + kCand) * 4 + 512 <= 160 * 1024, "select LDS exceeds a CU's 160 KB");
+static_assert(2 * ((kSelectLdsKeys + 31) / 32) <= kCand, "the two bitmaps must fit the candidate list");
 
 // Exclusive prefix over the lanes of a 64-bit ballot mask: the number of set lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
@@ -56,13 +57,11 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__restrict__ F, int N, int B,
-                                                                int32_t *__restrict__ kept)
+__global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const float *__restrict__ F, int N, int B,
+                                                                       int32_t *__restrict__ kept)
 {
     constexpr int NT = kSelectThreads;
     constexpr int NW = NT / 64;
-    extern __shared__ uint32_t keys[];                // [N] when IN_LDS
     __shared__ uint32_t hist[kBins0];
     __shared__ uint32_t cand[kCand];
     __shared__ uint32_t wa[NW], wb[NW];
@@ -73,44 +72,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform loop bounds
     const float *f = F + (size_t)sid * N;
     int32_t *out = kept + (size_t)sid * B;            // B < N on this path
-    if (IN_LDS) {
-        // eight independent loads in flight per thread (16-byte loads when the rows allow)
-        if ((N & 3) == 0 && ((uintptr_t)F & 15) == 0) {
-            const float4 *f4 = (const float4 *)f;
-            const int n4 = N >> 2;
-            for (int base = 0; base < n4; base += 8 * NT) {
-                float4 v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int i = base + u * NT + threadIdx.x;
-                    v[u] = i < n4 ? f4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int i = base + u * NT + threadIdx.x;
-                    if (i < n4)
-                        *(uint4 *)&keys[4 * i] = make_uint4(order_key(v[u].x), order_key(v[u].y), order_key(v[u].z),
-                                                            order_key(v[u].w));
-                }
-            }
-        } else {
-            for (int base = 0; base < N; base += 8 * NT) {
-                float v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = base + u * NT + threadIdx.x;
-                    v[u] = j < N ? f[j] : 0.f;
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = base + u * NT + threadIdx.x;
-                    if (j < N) keys[j] = order_key(v[u]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    auto key_at = [&](int j) -> uint32_t { return IN_LDS ? keys[j] : order_key(f[j]); };
+    auto key_at = [&](int j) -> uint32_t { return order_key(f[j]); };
     // wave w owns the contiguous key range [lo, hi); it walks it 256 keys per step, lane l taking
     // keys b + 64e + l (e < 4): four independent reads per step, visited in index order
     const int per = (N + NW - 1) / NW;
@@ -273,6 +235,206 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float *__r
     }
 }
 
+// Streams that fit in LDS: the same selection in four passes over the keys.
+//   1. load F, map to order keys into LDS and histogram digit 0 in the same pass;
+//   2. the keys of the chosen digit-0 bin go to the candidate list in any order (one LDS atomic
+//      per wave step reserves their slots): digits 1 and 2 only count them;
+//   3. each wave step of 64 keys stores two ballot masks, keys > T and keys == T, as bitmaps;
+//   4. thread w takes bitmap word w: a block-wide prefix of the words' population counts gives
+//      every kept key its slot, #(key > T before j) + min(#(key == T before j), k), and the
+//      thread writes the indices of its word's kept keys.
+// Passes 3 and 4 replace the count-then-write walks over all keys by one walk plus a walk over
+// N/32 words.
+__global__ __launch_bounds__(kSelectThreads) void select_lds_kernel(const float *__restrict__ F, int N, int B,
+                                                                    int32_t *__restrict__ kept)
+{
+    constexpr int NT = kSelectThreads;
+    constexpr int NW = NT / 64;
+    extern __shared__ uint32_t keys[];                // [N]
+    __shared__ uint32_t hist[kBins0];
+    __shared__ uint32_t cand[kCand];                  // candidates; afterwards the two bitmaps
+    __shared__ uint32_t scan[NW + 1];
+    __shared__ uint32_t s_prefix, s_k, s_ncand;
+
+    const int sid = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float *f = F + (size_t)sid * N;
+    int32_t *out = kept + (size_t)sid * B;            // B < N on this path
+
+    for (int i = threadIdx.x; i < kBins0; i += NT) hist[i] = 0u;
+    if (threadIdx.x == 0) s_ncand = 0u;
+    __syncthreads();
+
+    // ---- pass 1: order keys into LDS, histogram of digit 0 (bits 31..21)
+    if ((N & 3) == 0 && ((uintptr_t)F & 15) == 0) {
+        const float4 *f4 = (const float4 *)f;
+        const int n4 = N >> 2;
+        for (int base = 0; base < n4; base += 8 * NT) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = base + u * NT + threadIdx.x;
+                v[u] = i < n4 ? f4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = base + u * NT + threadIdx.x;
+                const bool in = i < n4;
+                const uint4 q = make_uint4(order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w));
+                if (in) *(uint4 *)&keys[4 * i] = q;
+                hist_add(hist, q.x >> 21, in);
+                hist_add(hist, q.y >> 21, in);
+                hist_add(hist, q.z >> 21, in);
+                hist_add(hist, q.w >> 21, in);
+            }
+        }
+    } else {
+        for (int base = 0; base < N; base += 8 * NT) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = base + u * NT + threadIdx.x;
+                v[u] = j < N ? f[j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = base + u * NT + threadIdx.x;
+                const uint32_t q = order_key(v[u]);
+                if (j < N) keys[j] = q;
+                hist_add(hist, q >> 21, j < N);
+            }
+        }
+    }
+
+    uint32_t prefix = 0u, mask = 0u, k = (uint32_t)B;
+    auto find_bin = [&](int shift, int nbins) {
+        __syncthreads();
+        if (wid == 0) {
+            const int per_lane = nbins / 64;
+            uint32_t local = 0u;
+            for (int i = 0; i < per_lane; ++i) local += hist[nbins - 1 - lane * per_lane - i];
+            const uint32_t incl = wave_incl_scan(local);
+            uint32_t excl = incl - local;
+            if (excl < k && k <= incl) {
+                for (int i = 0; i < per_lane; ++i) {
+                    const int bin = nbins - 1 - lane * per_lane - i;
+                    const uint32_t c = hist[bin];
+                    if (excl + c >= k) {
+                        s_prefix = prefix | ((uint32_t)bin << shift);
+                        s_k = k - excl;
+                        break;
+                    }
+                    excl += c;
+                }
+            }
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        k = s_k;
+    };
+    find_bin(21, kBins0);
+    mask = 0xffe00000u;
+
+    // ---- pass 2: candidates (keys whose digit 0 matches), in any order.  A wave step covers 256
+    // keys (four independent LDS reads per lane) and reserves its slots with one atomic.
+    const bool listed = hist[prefix >> 21] <= (uint32_t)kCand;   // uniform; read before hist is reused
+    if (listed) {
+        for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
+            uint32_t u[4];
+            uint64_t bal[4];
+            uint32_t tot = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 64 * e + lane;
+                u[e] = j < N ? keys[j] : 0u;
+                bal[e] = __ballot(j < N && (u[e] & mask) == prefix);
+                tot += (uint32_t)__builtin_popcountll(bal[e]);
+            }
+            if (tot) {
+                uint32_t base = 0u;
+                if (lane == 0) base = atomicAdd(&s_ncand, tot);
+                base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if ((bal[e] >> lane) & 1u) cand[base + lanes_below(bal[e])] = u[e];
+                    base += (uint32_t)__builtin_popcountll(bal[e]);
+                }
+            }
+        }
+    }
+    __syncthreads();                                  // candidates complete; hist is cleared next
+    const int ncand = (int)s_ncand;
+    for (int d = 1; d <= 2; ++d) {
+        const int shift = d == 1 ? 10 : 0;
+        const int nbins = d == 1 ? 2048 : 1024;
+        for (int i = threadIdx.x; i < nbins; i += NT) hist[i] = 0u;
+        __syncthreads();
+        if (listed) {
+            for (int base = 0; base < ncand; base += NT) {
+                const int i = base + threadIdx.x;
+                const uint32_t u = i < ncand ? cand[i] : 0u;
+                hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), i < ncand && (u & mask) == prefix);
+            }
+        } else {
+            for (int j0 = wid * 64; j0 < N; j0 += NT) {
+                const int j = j0 + lane;
+                const uint32_t u = j < N ? keys[j] : 0u;
+                hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), j < N && (u & mask) == prefix);
+            }
+        }
+        find_bin(shift, nbins);
+        mask |= (uint32_t)(nbins - 1) << shift;
+    }
+    const uint32_t T = prefix;   // the B-th largest key; k of the keys equal to T are kept
+
+    // ---- pass 3: bitmaps of keys > T and keys == T (word w holds keys 32w .. 32w + 31)
+    const int nwords = (N + 31) >> 5;
+    uint32_t *gtb = cand, *eqb = cand + nwords;       // the candidates are no longer needed
+    for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
+        // four 64-key chunks per step: eight bitmap words each for > T and == T, written by lanes 0..7
+        uint32_t wg = 0u, we = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 64 * e + lane;
+            const uint32_t u = j < N ? keys[j] : 0u;
+            const uint64_t mg = __ballot(j < N && u > T), me = __ballot(j < N && u == T);
+            if (lane == 2 * e) { wg = (uint32_t)mg; we = (uint32_t)me; }
+            if (lane == 2 * e + 1) { wg = (uint32_t)(mg >> 32); we = (uint32_t)(me >> 32); }
+        }
+        const int w = (j0 >> 5) + lane;
+        if (lane < 8 && w < nwords) {
+            gtb[w] = wg;
+            eqb[w] = we;
+        }
+    }
+    __syncthreads();
+
+    // ---- pass 4: slots from prefix counts over the words, then the kept indices
+    uint32_t gcarry = 0u, ecarry = 0u;
+    for (int w0 = 0; w0 < nwords; w0 += NT) {
+        const int w = w0 + threadIdx.x;
+        const uint32_t g = w < nwords ? gtb[w] : 0u, e = w < nwords ? eqb[w] : 0u;
+        // prefix of (popcount g, popcount e) packed as two 16-bit fields (each total < 65536)
+        const uint32_t x = (uint32_t)__builtin_popcount(g) | ((uint32_t)__builtin_popcount(e) << 16);
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan<NT>(x, scan, &tot);
+        const uint32_t gbase = gcarry + (ex & 0xffffu), ebase = ecarry + (ex >> 16);
+        uint32_t bits = g | e;
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const uint32_t below = (1u << b) - 1u;
+            const uint32_t ng = gbase + (uint32_t)__builtin_popcount(g & below);
+            const uint32_t ne = ebase + (uint32_t)__builtin_popcount(e & below);
+            const uint32_t slot = ((g >> b) & 1u) ? ng + min(ne, k) : (ne < k ? ng + ne : 0xffffffffu);
+            if (slot < (uint32_t)B) out[slot] = 32 * w + b;   // always true for a kept key
+        }
+        gcarry += tot & 0xffffu;
+        ecarry += tot >> 16;
+    }
+}
+
 __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -288,11 +450,11 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
         return hipGetLastError();
     }
     if (N <= kSelectLdsKeys) {
-        const hipError_t e = allow_dynamic_lds((const void *)select_kernel<true>, kSelectLdsKeys * 4);
+        const hipError_t e = allow_dynamic_lds((const void *)select_lds_kernel, kSelectLdsKeys * 4);
         if (e != hipSuccess) return e;
-        select_kernel<true><<<n_streams, kSelectThreads, (size_t)N * 4, st>>>(F, N, B, kept);
+        select_lds_kernel<<<n_streams, kSelectThreads, (size_t)N * 4, st>>>(F, N, B, kept);
     } else {
-        select_kernel<false><<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept);
+        select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept);
     }
     return hipGetLastError();
 }
