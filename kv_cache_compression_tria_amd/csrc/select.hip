@@ -50,6 +50,7 @@ constexpr int kBins0 = 2048;      // digit 0: the top 11 bits of the order key
 constexpr int kCand = 4096;       // candidate list (keys of the chosen digit-0 bin), in LDS
 static_assert(kSelectLdsKeys * 4 + (kBins0 + kCand) * 4 + 512 <= 160 * 1024, "select LDS exceeds a CU's 160 KB");
 static_assert(2 * ((kSelectLdsKeys + 31) / 32) <= kCand, "the two bitmaps must fit the candidate list");
+constexpr int kSelectShortKeys = 8192;   // streams up to this many keys: 256-thread blocks, 40 KB of LDS
 
 // Exclusive prefix over the lanes of a 64-bit ballot mask: the number of set lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
@@ -245,10 +246,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
 //      thread writes the indices of its word's kept keys.
 // Passes 3 and 4 replace the count-then-write walks over all keys by one walk plus a walk over
 // N/32 words.
-__global__ __launch_bounds__(kSelectThreads) void select_lds_kernel(const float *__restrict__ F, int N, int B,
-                                                                    int32_t *__restrict__ kept)
+template <int NT>   // 1024 threads for long streams, 256 for short ones (several blocks per CU)
+__global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
+                                                        int32_t *__restrict__ kept)
 {
-    constexpr int NT = kSelectThreads;
     constexpr int NW = NT / 64;
     extern __shared__ uint32_t keys[];                // [N]
     __shared__ uint32_t hist[kBins0];
@@ -449,10 +450,12 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
         identity_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(kept, n_streams, N);
         return hipGetLastError();
     }
-    if (N <= kSelectLdsKeys) {
-        const hipError_t e = allow_dynamic_lds((const void *)select_lds_kernel, kSelectLdsKeys * 4);
+    if (N <= kSelectShortKeys) {
+        select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept);
+    } else if (N <= kSelectLdsKeys) {
+        const hipError_t e = allow_dynamic_lds((const void *)select_lds_kernel<kSelectThreads>, kSelectLdsKeys * 4);
         if (e != hipSuccess) return e;
-        select_lds_kernel<<<n_streams, kSelectThreads, (size_t)N * 4, st>>>(F, N, B, kept);
+        select_lds_kernel<kSelectThreads><<<n_streams, kSelectThreads, (size_t)N * 4, st>>>(F, N, B, kept);
     } else {
         select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept);
     }
