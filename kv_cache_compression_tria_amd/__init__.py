@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
     """Load libtria.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # One HIP runtime per process: torch ships its own copy of the runtime libraries.  Loading
+        # torch first makes libtria.so bind to that copy; loaded the other way round, the second
+        # runtime to initialise finds no device.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m kv_cache_compression_tria_amd.build`")

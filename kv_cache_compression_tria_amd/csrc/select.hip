@@ -47,10 +47,19 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin, bool live
 }
 
 constexpr int kBins0 = 2048;      // digit 0: the top 11 bits of the order key
-constexpr int kCand = 4096;       // candidate list (keys of the chosen digit-0 bin), in LDS
-static_assert(kSelectLdsKeys * 4 + (kBins0 + kCand) * 4 + 512 <= 160 * 1024, "select LDS exceeds a CU's 160 KB");
-static_assert(2 * ((kSelectLdsKeys + 31) / 32) <= kCand, "the two bitmaps must fit the candidate list");
-constexpr int kSelectShortKeys = 8192;   // streams up to this many keys: 256-thread blocks, 40 KB of LDS
+constexpr int kCand = 4096;       // candidate list in LDS (keys in the global kernel, indices in the LDS one)
+constexpr int kSelectDigitBins = 256;    // the sample's histogram and the candidates' 8-bit digits
+constexpr int kSelectBitmapWords = 2 * ((kSelectLdsKeys + 31) / 32);
+static_assert(kSelectBitmapWords >= kBins0, "the fallback's digit-0 histogram lives in the bitmap words");
+static_assert(kSelectLdsKeys * 4 + (kSelectBitmapWords + kCand + kSelectDigitBins) * 4 + 512 <= 160 * 1024,
+              "select LDS exceeds a CU's 160 KB");
+constexpr int kSelectShortKeys = 8192;   // streams up to this many keys: 256-thread blocks, 57 KB of LDS
+
+// the score of an order key (inverse of order_key)
+__device__ __forceinline__ float key_float(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
 
 // Exclusive prefix over the lanes of a 64-bit ballot mask: the number of set lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
@@ -236,38 +245,47 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
     }
 }
 
-// Streams that fit in LDS: the same selection in four passes over the keys.
-//   1. load F, map to order keys into LDS and histogram digit 0 in the same pass;
-//   2. the keys of the chosen digit-0 bin go to the candidate list in any order (one LDS atomic
-//      per wave step reserves their slots): digits 1 and 2 only count them;
-//   3. each wave step of 64 keys stores two ballot masks, keys > T and keys == T, as bitmaps;
-//   4. thread w takes bitmap word w: a block-wide prefix of the words' population counts gives
-//      every kept key its slot, #(key > T before j) + min(#(key == T before j), k), and the
-//      thread writes the indices of its word's kept keys.
-// Passes 3 and 4 replace the count-then-write walks over all keys by one walk plus a walk over
-// N/32 words.
+// Streams that fit in LDS (up to 32768 keys): the keys are loaded once into LDS as order keys.
+// A sample of NT keys (every (N / NT)-th) brackets the threshold: a 256-bin histogram of the
+// sample, linear in the score between the sample's extremes, gives two bin edges lo <= hi whose
+// ranks are the expected sample rank of the B-th largest key, minus and plus 4.5 standard
+// deviations of that binomial count (plus 2).  One pass over all keys then counts the keys at or
+// above hi (all kept), lists the indices of the keys in [lo, hi) as candidates and stores the
+// "above" bitmap.  When the bracket holds the threshold (#above < B <= #above + #candidates) and
+// the candidates fit, four 8-bit radix digits over the candidates alone give the B-th largest key
+// T and the number k of keys equal to T that are kept, and the candidates' bits are set in the
+// two bitmaps (> T, == T).  Otherwise (a sample that misses, heavy ties, non-finite scores) three
+// radix digits (11, 11, 10 bits) run over all keys, followed by a bitmap pass.  Finally thread w
+// takes bitmap word w: a block-wide prefix of the words' bit counts places every kept index at
+// slot #(key > T before j) + min(#(key == T before j), k).
 template <int NT>   // 1024 threads for long streams, 256 for short ones (several blocks per CU)
 __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
                                                         int32_t *__restrict__ kept)
 {
     constexpr int NW = NT / 64;
     extern __shared__ uint32_t keys[];                // [N]
-    __shared__ uint32_t hist[kBins0];
-    __shared__ uint32_t cand[kCand];                  // candidates; afterwards the two bitmaps
+    __shared__ uint32_t bm[kSelectBitmapWords];       // the two bitmaps, or the fallback's histogram
+    __shared__ uint32_t cand[kCand];                  // candidate indices
+    __shared__ uint32_t dh[kSelectDigitBins];         // sample histogram, candidate digits
     __shared__ uint32_t scan[NW + 1];
-    __shared__ uint32_t s_prefix, s_k, s_ncand;
+    __shared__ float s_min[NW], s_max[NW];
+    __shared__ uint32_t s_prefix, s_k, s_ncand, s_nabove, s_lo, s_hi;
 
     const int sid = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float *f = F + (size_t)sid * N;
     int32_t *out = kept + (size_t)sid * B;            // B < N on this path
+    const int nwords = (N + 31) >> 5;
+    uint32_t *gtb = bm, *eqb = bm + nwords;
 
-    for (int i = threadIdx.x; i < kBins0; i += NT) hist[i] = 0u;
-    if (threadIdx.x == 0) s_ncand = 0u;
-    __syncthreads();
+    for (int i = threadIdx.x; i < kSelectDigitBins; i += NT) dh[i] = 0u;
+    if (threadIdx.x == 0) {
+        s_ncand = 0u;
+        s_nabove = 0u;
+    }
 
-    // ---- pass 1: order keys into LDS, histogram of digit 0 (bits 31..21)
+    // ---- pass 1: order keys into LDS
     if ((N & 3) == 0 && ((uintptr_t)F & 15) == 0) {
         const float4 *f4 = (const float4 *)f;
         const int n4 = N >> 2;
@@ -281,13 +299,9 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int i = base + u * NT + threadIdx.x;
-                const bool in = i < n4;
-                const uint4 q = make_uint4(order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w));
-                if (in) *(uint4 *)&keys[4 * i] = q;
-                hist_add(hist, q.x >> 21, in);
-                hist_add(hist, q.y >> 21, in);
-                hist_add(hist, q.z >> 21, in);
-                hist_add(hist, q.w >> 21, in);
+                if (i < n4)
+                    *(uint4 *)&keys[4 * i] = make_uint4(order_key(v[u].x), order_key(v[u].y), order_key(v[u].z),
+                                                        order_key(v[u].w));
             }
         }
     } else {
@@ -301,26 +315,27 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = base + u * NT + threadIdx.x;
-                const uint32_t q = order_key(v[u]);
-                if (j < N) keys[j] = q;
-                hist_add(hist, q >> 21, j < N);
+                if (j < N) keys[j] = order_key(v[u]);
             }
         }
     }
+    __syncthreads();
 
     uint32_t prefix = 0u, mask = 0u, k = (uint32_t)B;
-    auto find_bin = [&](int shift, int nbins) {
+    // wave 0 finds the bin of h (nbins bins, counted from the top) where the running count first
+    // reaches k; prefix gains the bin's digit at `shift`, and k becomes the rank within the bin
+    auto find_bin = [&](const uint32_t *h, int shift, int nbins) {
         __syncthreads();
         if (wid == 0) {
             const int per_lane = nbins / 64;
             uint32_t local = 0u;
-            for (int i = 0; i < per_lane; ++i) local += hist[nbins - 1 - lane * per_lane - i];
+            for (int i = 0; i < per_lane; ++i) local += h[nbins - 1 - lane * per_lane - i];
             const uint32_t incl = wave_incl_scan(local);
             uint32_t excl = incl - local;
             if (excl < k && k <= incl) {
                 for (int i = 0; i < per_lane; ++i) {
                     const int bin = nbins - 1 - lane * per_lane - i;
-                    const uint32_t c = hist[bin];
+                    const uint32_t c = h[bin];
                     if (excl + c >= k) {
                         s_prefix = prefix | ((uint32_t)bin << shift);
                         s_k = k - excl;
@@ -334,23 +349,93 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
         prefix = s_prefix;
         k = s_k;
     };
-    find_bin(21, kBins0);
-    mask = 0xffe00000u;
 
-    // ---- pass 2: candidates (keys whose digit 0 matches), in any order.  A wave step covers 256
-    // keys (four independent LDS reads per lane) and reserves its slots with one atomic.
-    const bool listed = hist[prefix >> 21] <= (uint32_t)kCand;   // uniform; read before hist is reused
-    if (listed) {
+    // ---- the bracket from a sample: its extremes, 256 linear bins, the bins of two sample ranks
+    const int S = min(N, NT);
+    const int stride = N / S;
+    const bool smp = (int)threadIdx.x < S;
+    const float sv = smp ? key_float(keys[threadIdx.x * stride]) : 0.f;
+    {
+        float lo = smp ? sv : INFINITY, hi = smp ? sv : -INFINITY;
+        if (smp && !isfinite(sv)) {
+            lo = -INFINITY;                           // a non-finite sample: no usable bracket
+            hi = INFINITY;
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, o, 64));
+            hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+        }
+        if (lane == 0) {
+            s_min[wid] = lo;
+            s_max[wid] = hi;
+        }
+    }
+    __syncthreads();
+    float smin = INFINITY, smax = -INFINITY;
+    for (int w = 0; w < NW; ++w) {
+        smin = fminf(smin, s_min[w]);
+        smax = fmaxf(smax, s_max[w]);
+    }
+    const float span = smax - smin;
+    bool ok = isfinite(span) && span > 0.f;           // uniform
+    if (ok) {
+        const float scale = (float)kSelectDigitBins / span;
+        hist_add(dh, (uint32_t)min(kSelectDigitBins - 1, max(0, (int)((sv - smin) * scale))), smp);
+        __syncthreads();
+        if (wid == 0) {
+            const float pf = (float)B / (float)N;
+            const float e = pf * (float)S;
+            const float d = 4.5f * sqrtf((float)S * pf * (1.f - pf)) + 2.f;
+            const uint32_t r_hi = (uint32_t)fmaxf(1.f, floorf(e - d));
+            const uint32_t r_lo = (uint32_t)fminf((float)S, ceilf(e + d));
+            constexpr int PL = kSelectDigitBins / 64;   // lane l owns bins 255 - PL*l downwards
+            uint32_t local = 0u;
+            for (int i = 0; i < PL; ++i) local += dh[kSelectDigitBins - 1 - lane * PL - i];
+            const uint32_t incl = wave_incl_scan(local);
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t r = t == 0 ? r_hi : r_lo;
+                uint32_t run = incl - local;
+                if (run < r && r <= incl) {
+                    for (int i = 0; i < PL; ++i) {
+                        const int bin = kSelectDigitBins - 1 - lane * PL - i;
+                        run += dh[bin];
+                        if (run >= r) {
+                            if (t == 0)
+                                s_hi = bin == kSelectDigitBins - 1 ? 0xffffffffu
+                                                                   : order_key(smin + (float)(bin + 1) / scale);
+                            else
+                                s_lo = order_key(smin + (float)bin / scale);
+                            break;
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- pass 2: keys at or above hi (counted, "above" bitmap), candidates in [lo, hi)
+    if (ok) {
+        const uint32_t lo = s_lo, hi = s_hi;
+        uint32_t nabove = 0u;
         for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
-            uint32_t u[4];
-            uint64_t bal[4];
-            uint32_t tot = 0u;
+            uint32_t wa = 0u, tot = 0u;
+            uint64_t bc[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = j0 + 64 * e + lane;
-                u[e] = j < N ? keys[j] : 0u;
-                bal[e] = __ballot(j < N && (u[e] & mask) == prefix);
-                tot += (uint32_t)__builtin_popcountll(bal[e]);
+                const uint32_t u = j < N ? keys[j] : 0u;
+                const uint64_t ma = __ballot(j < N && u >= hi);
+                bc[e] = __ballot(j < N && u >= lo && u < hi);
+                nabove += (uint32_t)__builtin_popcountll(ma);
+                tot += (uint32_t)__builtin_popcountll(bc[e]);
+                if (lane == 2 * e) wa = (uint32_t)ma;
+                if (lane == 2 * e + 1) wa = (uint32_t)(ma >> 32);
+            }
+            const int w = (j0 >> 5) + lane;
+            if (lane < 8 && w < nwords) {
+                gtb[w] = wa;
+                eqb[w] = 0u;
             }
             if (tot) {
                 uint32_t base = 0u;
@@ -358,60 +443,127 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
                 base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if ((bal[e] >> lane) & 1u) cand[base + lanes_below(bal[e])] = u[e];
-                    base += (uint32_t)__builtin_popcountll(bal[e]);
+                    if ((bc[e] >> lane) & 1u) {
+                        const uint32_t slot = base + lanes_below(bc[e]);
+                        if (slot < (uint32_t)kCand) cand[slot] = (uint32_t)(j0 + 64 * e + lane);
+                    }
+                    base += (uint32_t)__builtin_popcountll(bc[e]);
                 }
             }
         }
-    }
-    __syncthreads();                                  // candidates complete; hist is cleared next
-    const int ncand = (int)s_ncand;
-    for (int d = 1; d <= 2; ++d) {
-        const int shift = d == 1 ? 10 : 0;
-        const int nbins = d == 1 ? 2048 : 1024;
-        for (int i = threadIdx.x; i < nbins; i += NT) hist[i] = 0u;
+        if (lane == 0 && nabove) atomicAdd(&s_nabove, nabove);
         __syncthreads();
-        if (listed) {
-            for (int base = 0; base < ncand; base += NT) {
+        const uint32_t na = s_nabove, nc = s_ncand;
+        ok = na < (uint32_t)B && (uint32_t)B <= na + nc && nc <= (uint32_t)kCand;   // uniform
+    }
+
+    if (ok) {
+        // ---- the threshold among the candidates: four 8-bit digits
+        const int nc = (int)s_ncand;
+        k = (uint32_t)B - s_nabove;
+        for (int dgt = 0; dgt < 4; ++dgt) {
+            const int shift = 24 - 8 * dgt;
+            for (int i = threadIdx.x; i < kSelectDigitBins; i += NT) dh[i] = 0u;
+            __syncthreads();
+            for (int base = 0; base < nc; base += NT) {
                 const int i = base + threadIdx.x;
-                const uint32_t u = i < ncand ? cand[i] : 0u;
-                hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), i < ncand && (u & mask) == prefix);
+                const uint32_t u = i < nc ? keys[cand[i]] : 0u;
+                hist_add(dh, (u >> shift) & (uint32_t)(kSelectDigitBins - 1), i < nc && (u & mask) == prefix);
             }
-        } else {
-            for (int j0 = wid * 64; j0 < N; j0 += NT) {
-                const int j = j0 + lane;
-                const uint32_t u = j < N ? keys[j] : 0u;
-                hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), j < N && (u & mask) == prefix);
-            }
+            find_bin(dh, shift, kSelectDigitBins);
+            mask |= (uint32_t)(kSelectDigitBins - 1) << shift;
         }
-        find_bin(shift, nbins);
-        mask |= (uint32_t)(nbins - 1) << shift;
-    }
-    const uint32_t T = prefix;   // the B-th largest key; k of the keys equal to T are kept
-
-    // ---- pass 3: bitmaps of keys > T and keys == T (word w holds keys 32w .. 32w + 31)
-    const int nwords = (N + 31) >> 5;
-    uint32_t *gtb = cand, *eqb = cand + nwords;       // the candidates are no longer needed
-    for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
-        // four 64-key chunks per step: eight bitmap words each for > T and == T, written by lanes 0..7
-        uint32_t wg = 0u, we = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = j0 + 64 * e + lane;
+        const uint32_t T = prefix;
+        for (int i = threadIdx.x; i < nc; i += NT) {
+            const uint32_t j = cand[i], u = keys[j];
+            if (u > T) atomicOr(&gtb[j >> 5], 1u << (j & 31));
+            else if (u == T) atomicOr(&eqb[j >> 5], 1u << (j & 31));
+        }
+        __syncthreads();
+    } else {
+        // ---- fallback: digit 0 (bits 31..21) over all keys, candidates, digits 1 and 2
+        uint32_t *hist = bm;                          // kSelectBitmapWords >= kBins0
+        for (int i = threadIdx.x; i < kBins0; i += NT) hist[i] = 0u;
+        if (threadIdx.x == 0) s_ncand = 0u;
+        __syncthreads();
+        for (int j0 = wid * 64; j0 < N; j0 += NT) {
+            const int j = j0 + lane;
             const uint32_t u = j < N ? keys[j] : 0u;
-            const uint64_t mg = __ballot(j < N && u > T), me = __ballot(j < N && u == T);
-            if (lane == 2 * e) { wg = (uint32_t)mg; we = (uint32_t)me; }
-            if (lane == 2 * e + 1) { wg = (uint32_t)(mg >> 32); we = (uint32_t)(me >> 32); }
+            hist_add(hist, u >> 21, j < N);
         }
-        const int w = (j0 >> 5) + lane;
-        if (lane < 8 && w < nwords) {
-            gtb[w] = wg;
-            eqb[w] = we;
+        prefix = 0u;
+        k = (uint32_t)B;
+        find_bin(hist, 21, kBins0);
+        mask = 0xffe00000u;
+        const bool listed = hist[prefix >> 21] <= (uint32_t)kCand;   // uniform
+        if (listed) {
+            for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
+                uint64_t bal[4];
+                uint32_t tot = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + 64 * e + lane;
+                    const uint32_t u = j < N ? keys[j] : 0u;
+                    bal[e] = __ballot(j < N && (u & mask) == prefix);
+                    tot += (uint32_t)__builtin_popcountll(bal[e]);
+                }
+                if (tot) {
+                    uint32_t base = 0u;
+                    if (lane == 0) base = atomicAdd(&s_ncand, tot);
+                    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if ((bal[e] >> lane) & 1u) cand[base + lanes_below(bal[e])] = (uint32_t)(j0 + 64 * e + lane);
+                        base += (uint32_t)__builtin_popcountll(bal[e]);
+                    }
+                }
+            }
         }
+        __syncthreads();                              // candidates complete; hist is cleared next
+        const int nc = (int)s_ncand;
+        for (int dgt = 1; dgt <= 2; ++dgt) {
+            const int shift = dgt == 1 ? 10 : 0;
+            const int nbins = dgt == 1 ? 2048 : 1024;
+            for (int i = threadIdx.x; i < nbins; i += NT) hist[i] = 0u;
+            __syncthreads();
+            if (listed) {
+                for (int base = 0; base < nc; base += NT) {
+                    const int i = base + threadIdx.x;
+                    const uint32_t u = i < nc ? keys[cand[i]] : 0u;
+                    hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), i < nc && (u & mask) == prefix);
+                }
+            } else {
+                for (int j0 = wid * 64; j0 < N; j0 += NT) {
+                    const int j = j0 + lane;
+                    const uint32_t u = j < N ? keys[j] : 0u;
+                    hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), j < N && (u & mask) == prefix);
+                }
+            }
+            find_bin(hist, shift, nbins);
+            mask |= (uint32_t)(nbins - 1) << shift;
+        }
+        const uint32_t T = prefix;
+        // bitmaps over all keys (the histogram is no longer read: find_bin ended with a barrier)
+        for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
+            uint32_t wg = 0u, we = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 64 * e + lane;
+                const uint32_t u = j < N ? keys[j] : 0u;
+                const uint64_t mg = __ballot(j < N && u > T), me = __ballot(j < N && u == T);
+                if (lane == 2 * e) { wg = (uint32_t)mg; we = (uint32_t)me; }
+                if (lane == 2 * e + 1) { wg = (uint32_t)(mg >> 32); we = (uint32_t)(me >> 32); }
+            }
+            const int w = (j0 >> 5) + lane;
+            if (lane < 8 && w < nwords) {
+                gtb[w] = wg;
+                eqb[w] = we;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // ---- pass 4: slots from prefix counts over the words, then the kept indices
+    // ---- output: slots from prefix counts over the words, then the kept indices
     uint32_t gcarry = 0u, ecarry = 0u;
     for (int w0 = 0; w0 < nwords; w0 += NT) {
         const int w = w0 + threadIdx.x;
