@@ -2,20 +2,20 @@
 //
 // Keep the B keys with the largest final score, ties to the lower index, written in ascending
 // index order (chenxutan.com/d/2624 section 4.2: top-k of the scores, then sorted to keep the
-// cache order).  One workgroup of 16 waves per stream.  Scores are mapped to order-preserving
-// unsigned keys (-0 folded onto +0); three radix digits (11, 11 and 10 bits) find the B-th
-// largest key T and how many of the keys equal to T are kept (k): a histogram of digit 0 over all
-// keys picks a bin, the keys of that bin are copied to a candidate list, and digits 1 and 2 are
-// resolved over the candidates alone.  Final scores cluster in a few exponent values, so the top
-// digit piles onto few bins: each wave first counts its heavy bins with one ballot per bin and a
-// single atomic, and only the scattered rest use per-lane atomics.  Every key > T is kept and the
-// first k keys == T (in index order), at slot #(key > T before j) + min(#(key == T before j), k).
-//   select_lds_kernel (streams whose keys fit in LDS): the keys live in LDS; the candidates are
-//     listed in any order; the kept set is written as two bitmaps (> T, == T), and a prefix of the
-//     words' population counts places every kept index.
-//   select_global_kernel (longer streams): the keys are re-read from F in every pass; wave w owns
-//     the contiguous key range [w*N/16, (w+1)*N/16), and the candidate list and the output are
-//     written in index order from per-wave counts and a prefix over the 16 wave totals.
+// cache order).  One workgroup per stream.  Scores are mapped to order-preserving unsigned keys
+// (-0 folded onto +0); the B-th largest key T and the number k of keys equal to T that are kept
+// are found by radix digits over LDS histograms.  Final scores cluster in a few exponent values,
+// so a digit can pile onto few bins: each wave first counts its heavy bins with one ballot per
+// bin and a single atomic, and only the scattered rest use per-lane atomics.  Every key > T is
+// kept and the first k keys == T (in index order), at slot
+// #(key > T before j) + min(#(key == T before j), k).
+//   select_stream_kernel (streams of 8193 to 32768 keys): brackets T from a sample, passes over F
+//     once, resolves T among the bracketed keys and writes the output from two bitmaps;
+//   select_lds_kernel (streams up to 8192 keys): the same steps over an LDS copy of the keys;
+//   select_global_kernel (longer streams): three digits (11, 11, 10 bits) over all keys re-read
+//     from F in every pass; wave w owns the contiguous key range [w*N/16, (w+1)*N/16), and the
+//     candidate list and the output are written in index order from per-wave counts and a prefix
+//     over the 16 wave totals.
 #include "common.cuh"
 #include "tria_internal.h"
 
@@ -47,13 +47,17 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin, bool live
 }
 
 constexpr int kBins0 = 2048;      // digit 0: the top 11 bits of the order key
-constexpr int kCand = 4096;       // candidate list in LDS (keys in the global kernel, indices in the LDS one)
-constexpr int kSelectDigitBins = 256;    // the sample's histogram and the candidates' 8-bit digits
-constexpr int kSelectBitmapWords = 2 * ((kSelectLdsKeys + 31) / 32);
-static_assert(kSelectBitmapWords >= kBins0, "the fallback's digit-0 histogram lives in the bitmap words");
-static_assert(kSelectLdsKeys * 4 + (kSelectBitmapWords + kCand + kSelectDigitBins) * 4 + 512 <= 160 * 1024,
-              "select LDS exceeds a CU's 160 KB");
-constexpr int kSelectShortKeys = 8192;   // streams up to this many keys: 256-thread blocks, 57 KB of LDS
+constexpr int kCand = 4096;       // candidate list in LDS
+constexpr int kSelectDigitBins = 256;    // the sample's histogram and the bracketed keys' 8-bit digits
+constexpr int kSelectBitmapWords = 2 * ((kSelectStreamKeys + 31) / 32);
+constexpr int kSelectShortKeys = 8192;   // streams up to this many keys: LDS copy, 256-thread blocks
+constexpr int kSelectSamples = 1024;     // sampled scores behind the bracket
+static_assert(kCand >= kBins0, "the fallback's histogram lives in the candidate keys");
+static_assert(kSelectBitmapWords >= kBins0, "the LDS selection's fallback histogram lives in the bitmap words");
+static_assert(kSelectShortKeys * 4 + (kSelectBitmapWords + kCand + kSelectDigitBins) * 4 + 1024 <= 64 * 1024,
+              "the LDS selection exceeds 64 KB without a dynamic-LDS attribute");
+static_assert((kSelectBitmapWords + 2 * kCand + kSelectDigitBins) * 4 + 1024 <= 64 * 1024,
+              "the streamed selection's static LDS exceeds 64 KB");
 
 // the score of an order key (inverse of order_key)
 __device__ __forceinline__ float key_float(uint32_t u)
@@ -245,7 +249,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
     }
 }
 
-// Streams that fit in LDS (up to 32768 keys): the keys are loaded once into LDS as order keys.
+// Short streams (up to 8192 keys) keep their keys in LDS: loaded once as order keys, then the same
+// steps as the streamed selection below, reading LDS instead of F.
 // A sample of NT keys (every (N / NT)-th) brackets the threshold: a 256-bin histogram of the
 // sample, linear in the score between the sample's extremes, gives two bin edges lo <= hi whose
 // ranks are the expected sample rank of the B-th largest key, minus and plus 4.5 standard
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
 // radix digits (11, 11, 10 bits) run over all keys, followed by a bitmap pass.  Finally thread w
 // takes bitmap word w: a block-wide prefix of the words' bit counts places every kept index at
 // slot #(key > T before j) + min(#(key == T before j), k).
-template <int NT>   // 1024 threads for long streams, 256 for short ones (several blocks per CU)
+template <int NT>
 __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
                                                         int32_t *__restrict__ kept)
 {
@@ -588,6 +593,303 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
     }
 }
 
+// Streams up to 32768 keys are selected straight from F (no LDS copy of the keys, 42 KB of LDS, so
+// several streams run per CU and hide each other's memory latency):
+//   1. a strided sample of 1024 scores brackets the threshold: a 256-bin histogram of the sample,
+//      linear in the score between its extremes, gives the bins of the sample ranks e -/+ (4.5
+//      sigma + 2) from the top, where e = S B / N is the expected rank of the B-th largest key and
+//      sigma the spread of that binomial count; their edges are the bounds lo <= hi;
+//   2. one pass over F (16-byte loads, four keys per lane) counts the keys at or above hi (all
+//      kept) and writes their bitmap, and lists the keys in [lo, hi) with their indices;
+//   3. when the bracket holds the threshold (#above < B <= #above + #listed) and the list fits,
+//      four 8-bit radix digits over the listed keys give the B-th largest key T and the number k
+//      of keys equal to T that are kept, and the listed keys' bits are set in the two bitmaps
+//      (> T, == T); otherwise (a sample that misses, heavy ties, an outlier stretching the bins,
+//      non-finite scores) three radix digits (11, 11, 10 bits) run over all keys, each pass
+//      re-reading F, and a bitmap pass follows;
+//   4. thread w takes bitmap word w: a block-wide prefix of the words' bit counts places every
+//      kept index at #(key > T before j) + min(#(key == T before j), k).
+template <int NT>
+__global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
+                                                           int32_t *__restrict__ kept)
+{
+    constexpr int NW = NT / 64;
+    constexpr int SMAX = kSelectSamples;
+    constexpr int SPT = (SMAX + NT - 1) / NT;         // samples per thread
+    __shared__ uint32_t bm[kSelectBitmapWords];       // the two bitmaps
+    __shared__ uint32_t ckey[kCand], cidx[kCand];     // candidates; the fallback's histogram in ckey
+    __shared__ uint32_t dh[kSelectDigitBins];
+    __shared__ uint32_t scan[NW + 1];
+    __shared__ float s_min[NW], s_max[NW];
+    __shared__ uint32_t s_prefix, s_k, s_ncand, s_nabove, s_lo, s_hi;
+
+    const int sid = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float *f = F + (size_t)sid * N;
+    int32_t *out = kept + (size_t)sid * B;            // B < N on this path
+    const int nwords = (N + 31) >> 5;
+    uint32_t *gtb = bm, *eqb = bm + nwords;
+
+    for (int i = threadIdx.x; i < kSelectDigitBins; i += NT) dh[i] = 0u;
+    if (threadIdx.x == 0) {
+        s_ncand = 0u;
+        s_nabove = 0u;
+    }
+
+    uint32_t prefix = 0u, mask = 0u, k = (uint32_t)B;
+    auto find_bin = [&](const uint32_t *h, int shift, int nbins) {
+        __syncthreads();
+        if (wid == 0) {
+            const int per_lane = nbins / 64;
+            uint32_t local = 0u;
+            for (int i = 0; i < per_lane; ++i) local += h[nbins - 1 - lane * per_lane - i];
+            const uint32_t incl = wave_incl_scan(local);
+            uint32_t excl = incl - local;
+            if (excl < k && k <= incl) {
+                for (int i = 0; i < per_lane; ++i) {
+                    const int bin = nbins - 1 - lane * per_lane - i;
+                    const uint32_t c = h[bin];
+                    if (excl + c >= k) {
+                        s_prefix = prefix | ((uint32_t)bin << shift);
+                        s_k = k - excl;
+                        break;
+                    }
+                    excl += c;
+                }
+            }
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        k = s_k;
+    };
+
+    // ---- the bracket from a strided sample of the scores
+    const int S = min(N, SMAX);
+    const int stride = N / S;
+    float sv[SPT];
+    bool smp[SPT];
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) {
+        const int t = q * NT + threadIdx.x;
+        smp[q] = t < S;
+        sv[q] = smp[q] ? f[(size_t)t * stride] : 0.f;
+        if (smp[q]) {
+            if (isfinite(sv[q])) {
+                lo = fminf(lo, sv[q]);
+                hi = fmaxf(hi, sv[q]);
+            } else {
+                lo = -INFINITY;                       // a non-finite sample: no usable bracket
+                hi = INFINITY;
+            }
+        }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, o, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    if (lane == 0) {
+        s_min[wid] = lo;
+        s_max[wid] = hi;
+    }
+    __syncthreads();
+    float smin = INFINITY, smax = -INFINITY;
+    for (int w = 0; w < NW; ++w) {
+        smin = fminf(smin, s_min[w]);
+        smax = fmaxf(smax, s_max[w]);
+    }
+    const float span = smax - smin;
+    bool ok = isfinite(span) && span > 0.f;           // uniform
+    if (ok) {
+        const float scale = (float)kSelectDigitBins / span;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q)
+            hist_add(dh, (uint32_t)min(kSelectDigitBins - 1, max(0, (int)((sv[q] - smin) * scale))), smp[q]);
+        __syncthreads();
+        if (wid == 0) {
+            const float pf = (float)B / (float)N;
+            const float e = pf * (float)S;
+            const float d = 4.5f * sqrtf((float)S * pf * (1.f - pf)) + 2.f;
+            const uint32_t r_hi = (uint32_t)fmaxf(1.f, floorf(e - d));
+            const uint32_t r_lo = (uint32_t)fminf((float)S, ceilf(e + d));
+            constexpr int PL = kSelectDigitBins / 64;
+            uint32_t local = 0u;
+            for (int i = 0; i < PL; ++i) local += dh[kSelectDigitBins - 1 - lane * PL - i];
+            const uint32_t incl = wave_incl_scan(local);
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t r = t == 0 ? r_hi : r_lo;
+                uint32_t run = incl - local;
+                if (run < r && r <= incl) {
+                    for (int i = 0; i < PL; ++i) {
+                        const int bin = kSelectDigitBins - 1 - lane * PL - i;
+                        run += dh[bin];
+                        if (run >= r) {
+                            if (t == 0)
+                                s_hi = bin == kSelectDigitBins - 1 ? 0xffffffffu
+                                                                   : order_key(smin + (float)(bin + 1) / scale);
+                            else
+                                s_lo = order_key(smin + (float)bin / scale);
+                            break;
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- one pass over F: keys at or above hi (counted, bitmap), candidates in [lo, hi)
+    const bool vec = (N & 3) == 0 && ((uintptr_t)F & 15) == 0;   // uniform
+    if (ok) {
+        const uint32_t blo = s_lo, bhi = s_hi;
+        uint32_t nabove = 0u;
+        // a wave step covers 256 keys: lane l holds keys 4l .. 4l + 3 of the step
+        for (int c0 = wid * 256; c0 < N; c0 += NT * 4) {
+            uint32_t u[4];
+            if (vec) {
+                const int i4 = (c0 >> 2) + lane;
+                const float4 v = 4 * i4 < N ? ((const float4 *)f)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                u[0] = order_key(v.x); u[1] = order_key(v.y); u[2] = order_key(v.z); u[3] = order_key(v.w);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = c0 + 4 * lane + e;
+                    u[e] = j < N ? order_key(f[j]) : 0u;
+                }
+            }
+            uint32_t nib = 0u;
+            uint64_t bc[4];
+            uint32_t tot = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = c0 + 4 * lane + e;
+                const bool in = j < N;
+                const bool ab = in && u[e] >= bhi;
+                nib |= (uint32_t)ab << e;
+                bc[e] = __ballot(in && u[e] >= blo && u[e] < bhi);
+                tot += (uint32_t)__builtin_popcountll(bc[e]);
+                nabove += (uint32_t)__builtin_popcountll(__ballot(ab));
+            }
+            // eight lanes make one bitmap word (32 keys); lane 8m writes word c0/32 + m
+            uint32_t word = nib << (4 * (lane & 7));
+            word |= __shfl_xor(word, 1, 64);
+            word |= __shfl_xor(word, 2, 64);
+            word |= __shfl_xor(word, 4, 64);
+            const int w = (c0 >> 5) + (lane >> 3);
+            if ((lane & 7) == 0 && w < nwords) {
+                gtb[w] = word;
+                eqb[w] = 0u;
+            }
+            if (tot) {
+                uint32_t base = 0u;
+                if (lane == 0) base = atomicAdd(&s_ncand, tot);
+                base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if ((bc[e] >> lane) & 1u) {
+                        const uint32_t slot = base + lanes_below(bc[e]);
+                        if (slot < (uint32_t)kCand) {
+                            ckey[slot] = u[e];
+                            cidx[slot] = (uint32_t)(c0 + 4 * lane + e);
+                        }
+                    }
+                    base += (uint32_t)__builtin_popcountll(bc[e]);
+                }
+            }
+        }
+        if (lane == 0 && nabove) atomicAdd(&s_nabove, nabove);
+        __syncthreads();
+        const uint32_t na = s_nabove, nc = s_ncand;
+        ok = na < (uint32_t)B && (uint32_t)B <= na + nc && nc <= (uint32_t)kCand;   // uniform
+    }
+
+    if (ok) {
+        // ---- the threshold among the candidates: four 8-bit digits
+        const int nc = (int)s_ncand;
+        k = (uint32_t)B - s_nabove;
+        for (int dgt = 0; dgt < 4; ++dgt) {
+            const int shift = 24 - 8 * dgt;
+            for (int i = threadIdx.x; i < kSelectDigitBins; i += NT) dh[i] = 0u;
+            __syncthreads();
+            for (int base = 0; base < nc; base += NT) {
+                const int i = base + threadIdx.x;
+                const uint32_t u = i < nc ? ckey[i] : 0u;
+                hist_add(dh, (u >> shift) & (uint32_t)(kSelectDigitBins - 1), i < nc && (u & mask) == prefix);
+            }
+            find_bin(dh, shift, kSelectDigitBins);
+            mask |= (uint32_t)(kSelectDigitBins - 1) << shift;
+        }
+        const uint32_t T = prefix;
+        for (int i = threadIdx.x; i < nc; i += NT) {
+            const uint32_t j = cidx[i], u = ckey[i];
+            if (u > T) atomicOr(&gtb[j >> 5], 1u << (j & 31));
+            else if (u == T) atomicOr(&eqb[j >> 5], 1u << (j & 31));
+        }
+        __syncthreads();
+    } else {
+        // ---- fallback: three radix digits (11, 11, 10 bits) over all keys, re-read from F
+        uint32_t *hist = ckey;                        // kCand >= kBins0
+        prefix = 0u;
+        mask = 0u;
+        k = (uint32_t)B;
+        for (int dgt = 0; dgt < 3; ++dgt) {
+            const int shift = dgt == 0 ? 21 : dgt == 1 ? 10 : 0;
+            const int nbins = dgt == 2 ? 1024 : 2048;
+            for (int i = threadIdx.x; i < nbins; i += NT) hist[i] = 0u;
+            __syncthreads();
+            for (int j0 = wid * 64; j0 < N; j0 += NT) {
+                const int j = j0 + lane;
+                const uint32_t u = j < N ? order_key(f[j]) : 0u;
+                hist_add(hist, (u >> shift) & (uint32_t)(nbins - 1), j < N && (u & mask) == prefix);
+            }
+            find_bin(hist, shift, nbins);
+            mask |= (uint32_t)(nbins - 1) << shift;
+        }
+        const uint32_t T = prefix;
+        for (int j0 = wid * 256; j0 < N; j0 += NT * 4) {
+            uint32_t wg = 0u, we = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 64 * e + lane;
+                const uint32_t u = j < N ? order_key(f[j]) : 0u;
+                const uint64_t mg = __ballot(j < N && u > T), me = __ballot(j < N && u == T);
+                if (lane == 2 * e) { wg = (uint32_t)mg; we = (uint32_t)me; }
+                if (lane == 2 * e + 1) { wg = (uint32_t)(mg >> 32); we = (uint32_t)(me >> 32); }
+            }
+            const int w = (j0 >> 5) + lane;
+            if (lane < 8 && w < nwords) {
+                gtb[w] = wg;
+                eqb[w] = we;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- output: slots from prefix counts over the words, then the kept indices
+    uint32_t gcarry = 0u, ecarry = 0u;
+    for (int w0 = 0; w0 < nwords; w0 += NT) {
+        const int w = w0 + threadIdx.x;
+        const uint32_t g = w < nwords ? gtb[w] : 0u, e = w < nwords ? eqb[w] : 0u;
+        const uint32_t x = (uint32_t)__builtin_popcount(g) | ((uint32_t)__builtin_popcount(e) << 16);
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan<NT>(x, scan, &tot);
+        const uint32_t gbase = gcarry + (ex & 0xffffu), ebase = ecarry + (ex >> 16);
+        uint32_t bits = g | e;
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const uint32_t below = (1u << b) - 1u;
+            const uint32_t ng = gbase + (uint32_t)__builtin_popcount(g & below);
+            const uint32_t ne = ebase + (uint32_t)__builtin_popcount(e & below);
+            const uint32_t slot = ((g >> b) & 1u) ? ng + min(ne, k) : (ne < k ? ng + ne : 0xffffffffu);
+            if (slot < (uint32_t)B) out[slot] = 32 * w + b;   // always true for a kept key
+        }
+        gcarry += tot & 0xffffu;
+        ecarry += tot >> 16;
+    }
+}
+
 __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -604,10 +906,8 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
     }
     if (N <= kSelectShortKeys) {
         select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept);
-    } else if (N <= kSelectLdsKeys) {
-        const hipError_t e = allow_dynamic_lds((const void *)select_lds_kernel<kSelectThreads>, kSelectLdsKeys * 4);
-        if (e != hipSuccess) return e;
-        select_lds_kernel<kSelectThreads><<<n_streams, kSelectThreads, (size_t)N * 4, st>>>(F, N, B, kept);
+    } else if (N <= kSelectStreamKeys) {
+        select_stream_kernel<512><<<n_streams, 512, 0, st>>>(F, N, B, kept);
     } else {
         select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept);
     }

@@ -46,8 +46,8 @@ constexpr int kFusedLdsMax = 80 * 1024;   // raw scores of a stream kept on chip
 constexpr int kClusterLds = 128 * 1024;   // raw scores one block of a stream cluster keeps on chip
 constexpr int kClusterMaxBlocks = 1024;   // largest cluster grid the workspace has room for
 constexpr int kSelectThreads = 1024;
-constexpr int kSelectLdsKeys = 32768;     // streams up to this many keys are selected from LDS (128 KB of keys
-                                          // and 25 KB of static LDS: within the 160 KB of a CU)
+constexpr int kSelectStreamKeys = 32768;  // streams up to this many keys: the streamed selection (bitmaps of
+                                          // 2 x N/32 words in LDS)
 constexpr int kCompactThreads = 256;
 constexpr int kCompactRows = 64;
 
