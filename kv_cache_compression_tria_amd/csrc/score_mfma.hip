@@ -833,6 +833,278 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
     finish(rounds - 1);
 }
 
+// ---- staged cluster path: the keys reach LDS by direct memory-to-LDS loads -------------------
+// The same stream clusters, round protocol and on-chip raw scores as above, with the key tiles
+// fetched by global_load_lds_dwordx4 with the non-temporal hint instead of into registers: each
+// load instruction covers 1 KB of consecutive key bytes (four whole rows), which streams from HBM
+// faster than the matrix-core operand layout does, and the operands are then read from LDS.  Chunk
+// c of row r of a tile sits at slot 16 r + (c ^ r), so the operand reads (row j, chunk
+// 4 kb + g for lane (g, j)) hit distinct bank groups.  Each wave owns two 4 KB slots: the tile of
+// item i + 1 is in flight while item i is scored.  The compiler does not see these loads, so the
+// kernel waits for them itself (vmcnt counts them in issue order) and issues no other wave-local
+// vector-memory load between a tile's load and its wait except where it waits for everything.
+// The raw scores of a round take at most 64 KB of LDS (2048 keys at G = 8), so a stream of 32768
+// keys spans a cluster of 16 blocks.  The arrival of a round is counted after the next round's
+// first ring wait, which covers the partial sums' stores, instead of draining the loads in flight.
+constexpr int kStageLds = 64 * 1024;   // raw scores of one block's part of a stream
+constexpr int kStageDefer = 16;        // items scored before the previous round is finished
+
+// one 16-byte-per-lane memory-to-LDS load: lane l's 16 bytes at `src` land at lds_base + 16 l
+__device__ __forceinline__ void dma16(const u32x4 *src, const u32x4 *lds_base)
+{
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(la)
+                 : "memory", "m0");
+}
+
+template <int G>
+__global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
+    int streams, int Ps, int Kb, int cpx, int C, double *__restrict__ xpart, uint32_t *__restrict__ arrive,
+    float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats, int *__restrict__ err)
+{
+    constexpr int NW = kClusterWaves;
+    constexpr int GP = (G + 1) & ~1;
+    extern __shared__ float lraw[];                // [Kb][GP]
+    __shared__ u32x4 stg[NW][2][256];              // two 4 KB key-tile slots per wave
+    __shared__ BlockSumsT<NW> bs;
+    __shared__ float zmu[8], zinv[8];
+    __shared__ __attribute__((aligned(16))) double xs[32 * 8 * 4];   // the cluster's partials of a round
+    __shared__ u32x4 ops_l[kOps * 64];             // the next stream's operand words ...
+    __shared__ float piv_l[8];                     // ... and pivots, loaded into LDS during a round
+    static_assert(NW == kOps, "one 1 KB operand load per wave");
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    const int cl = x * cpx + y / Ps, part = y % Ps;
+    const int rounds = cl < streams ? (streams - cl + C - 1) / C : 0;
+    if (rounds == 0) return;                       // the whole cluster has no stream
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jj = lane & 15, grp = lane >> 4, ha = head_a(grp);
+    const int j0 = part * Kb;
+    const int nkeys = max(0, min(Kb, N - j0));
+    const int ntiles16 = (nkeys + 15) >> 4;
+    const int nt = max(1, (ntiles16 + NW - 1) / NW);   // items per wave and round
+    const int total = rounds * nt;
+
+    WaveScorer<G> ws;
+    ws.begin(ops, pivot, cl);
+    // the operand loads complete here, before the first memory-to-LDS load is counted
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) hold(__builtin_bit_cast(uint4, ws.c.at[kb]));
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) hold(__builtin_bit_cast(uint4, ws.c.an[a][h]));
+    hold(__builtin_bit_cast(uint32_t, ws.p[0]));
+    hold(__builtin_bit_cast(uint32_t, ws.p[1]));
+
+    // item i of this wave: tile wid + NW * (i mod nt) of stream cl + (i / nt) C, into slot i & 1;
+    // rows at or past the tile's valid count load row 0 (always a real row) and score nothing
+    auto load_item = [&](int i) {
+        const int ic = min(i, total - 1);
+        const int r = ic / nt;
+        const int sid = cl + r * C;
+        const int t = min(wid + NW * (ic - r * nt), ntiles16 - 1);
+        const u32x4 *base = t >= 0 ? k + ((size_t)sid * N + j0 + t * 16) * 16 : k + (size_t)sid * N * 16;
+        const int valid = t >= 0 ? nkeys - t * 16 : 0;
+        const u32x4 *slot = &stg[wid][i & 1][0];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int row = 4 * m + (lane >> 4);
+            dma16(base + (row < valid ? row : 0) * 16 + ((lane & 15) ^ row), slot + 64 * m);
+        }
+    };
+    // wait until every memory-to-LDS load but the newest tile's (4 instructions) has landed
+    auto wait_ring = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
+    auto read_item = [&](int i, u32x4 (&b)[4]) {
+        const u32x4 *slot = &stg[wid][i & 1][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) b[kb] = slot[jj * 16 + ((4 * kb + grp) ^ jj)];
+    };
+    auto put = [&](int li, const float (&v)[2]) {
+        const int key = (wid + NW * li) * 16 + jj;
+        if (key < nkeys) {
+            if (ha < GP) lraw[key * GP + ha] = v[0];
+            if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
+        }
+    };
+    // score item i (item li of its round) into v: its tile was loaded one item earlier
+    auto score_item = [&](int i, int li, float (&v)[2]) {
+        load_item(i + 1);
+        wait_ring();
+        u32x4 b[4];
+        read_item(i, b);
+        ws.score(b, nkeys - (wid + NW * li) * 16, v);
+    };
+    // round r's partial sums: wave 0 stores its block's per-head sums as agent-scope atomics; the
+    // arrival is counted by count_arrival once a ring wait has covered the stores
+    auto publish = [&](int r) {
+        if (wid != 0) return;
+        double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
+        if (lane < G) {
+            const Sums t2 = block_sums_of(bs, lane);
+            double *q = xr + ((size_t)part * G + lane) * 4;
+            __hip_atomic_store(q + 0, t2.s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 1, t2.s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 2, (double)t2.mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 3, (double)t2.mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    auto count_arrival = [&]() {
+        if (wid == 0 && lane == 0) __hip_atomic_fetch_add(&arrive[cl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto finish = [&](int r) {
+        const int sid = cl + r * C;
+        if (wid == 0) {
+            const double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
+            if (lane == 0) {
+                const uint32_t target = (uint32_t)(r + 1) * (uint32_t)Ps;
+                unsigned spins = 0;
+                while (__hip_atomic_load(&arrive[cl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                    if (++spins > kSpinLimit ||
+                        (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2)) {
+                        atomicOr(err, 2);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            // every partial of the round (lane q takes partials q, q + 64, ... of Ps G <= 256; the
+            // rest re-read the last) and the pivots (lanes h < G) in one batch of coherent loads,
+            // waited for once
+            const int nq = Ps * G;
+            const uint32_t *xq[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                xq[it] = (const uint32_t *)(xr + (size_t)min(lane + 64 * it, nq - 1) * 4);
+            const float *pv = pivot + (size_t)sid * G + min(lane, G - 1);
+            u32x4 w[4][2];
+            float pvv;
+            asm volatile(
+                "global_load_dwordx4 %0, %9, off sc1\n\t"
+                "global_load_dwordx4 %1, %9, off offset:16 sc1\n\t"
+                "global_load_dwordx4 %2, %10, off sc1\n\t"
+                "global_load_dwordx4 %3, %10, off offset:16 sc1\n\t"
+                "global_load_dwordx4 %4, %11, off sc1\n\t"
+                "global_load_dwordx4 %5, %11, off offset:16 sc1\n\t"
+                "global_load_dwordx4 %6, %12, off sc1\n\t"
+                "global_load_dwordx4 %7, %12, off offset:16 sc1\n\t"
+                "global_load_dword %8, %13, off\n\t"
+                "s_waitcnt vmcnt(0)"
+                : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[1][0]), "=&v"(w[1][1]), "=&v"(w[2][0]), "=&v"(w[2][1]),
+                  "=&v"(w[3][0]), "=&v"(w[3][1]), "=&v"(pvv)
+                : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(pv)
+                : "memory");
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int q = lane + 64 * it;
+                if (q < nq) {
+                    u32x4 *dst = (u32x4 *)(xs + (size_t)q * 4);
+                    dst[0] = w[it][0];
+                    dst[1] = w[it][1];
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_wave_barrier();
+            if (lane < G) {
+                const int h = lane;
+                Sums t2;
+                t2.init();
+                for (int pp = 0; pp < Ps; ++pp) {
+                    const double *q = xs + ((size_t)pp * G + h) * 4;
+                    Sums u;
+                    u.s1 = q[0]; u.s2 = q[1]; u.mn = (float)q[2]; u.mx = (float)q[3];
+                    t2.add(u);
+                }
+                double mean, sd;
+                finish_moments(t2, (double)pvv, (double)N, mean, sd);
+                zmu[h] = (float)mean;
+                zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
+                if (part == 0) {
+                    if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
+                    if (stats) {
+                        stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
+                        stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        float *fo = F + (size_t)sid * N + j0;
+        for (int j = threadIdx.x; j < nkeys; j += NW * 64) {
+            float z = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[j * GP + h] - zmu[h]) * zinv[h]);
+            fo[j] = z;
+        }
+        if (raw_out)
+            for (int q = threadIdx.x; q < G * nkeys; q += NW * 64) {
+                const int h = q / nkeys, j = q - h * nkeys;
+                raw_out[((size_t)sid * G + h) * N + j0 + j] = lraw[j * GP + h];
+            }
+        __syncthreads();                           // LDS raw and zmu are reused
+    };
+
+    load_item(0);
+    for (int r = 0; r < rounds; ++r) {
+        int li = 0;
+        if (r > 0) {
+            // The first items of a round keep their scores in registers while the previous round
+            // is finished (its wait for the slowest block is covered by scoring).  The round's
+            // last item always runs below, where it brings in the next stream's operands.  The
+            // previous round's arrival is counted after the first item's ring wait, which covers
+            // the partial sums' stores; without such an item, after waiting for everything.
+            const int nd = min(kStageDefer, nt - 1);
+            float dv[kStageDefer][2];
+#pragma unroll
+            for (int q = 0; q < kStageDefer; ++q) {
+                if (q < nd) {
+                    score_item(r * nt + q, q, dv[q]);
+                    if (q == 0) count_arrival();
+                }
+            }
+            if (nd == 0) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                count_arrival();
+            }
+            finish(r - 1);
+#pragma unroll
+            for (int q = 0; q < kStageDefer; ++q)
+                if (q < nd) put(q, dv[q]);
+            li = nd;
+        }
+        const bool more = r + 1 < rounds;
+        for (; li < nt; ++li) {
+            if (li == nt - 1 && more) {
+                // the next stream's operand words (1 KB per wave) and pivots, loaded into LDS
+                // ahead of this item's tile, so that this item's ring wait covers them
+                const int sn = cl + (r + 1) * C;
+                dma16(ops + (size_t)sn * kOps * 64 + wid * 64 + lane, &ops_l[wid * 64]);
+                if (wid == 0 && lane < G) {
+                    const uint32_t la = __builtin_amdgcn_readfirstlane(
+                        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)piv_l);
+                    const float *src = pivot + (size_t)sn * G + lane;   // lane l -> piv_l[l]
+                    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la)
+                                 : "memory", "m0");
+                }
+            }
+            float v[2];
+            score_item(r * nt + li, li, v);
+            put(li, v);
+        }
+        // ---- end of round r: stage and publish the partial sums, switch to the next stream
+        block_sums_stage(bs, ws.m);
+        __syncthreads();
+        publish(r);
+        if (more) ws.begin_lds(ops_l, piv_l);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last round's stores and tile loads
+    count_arrival();
+    finish(rounds - 1);
+}
+
 __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int n, uint32_t v)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -901,6 +1173,61 @@ static hipError_t launch_cluster_g(const ClusterPlan &pl, const u32x4 *kp, const
     KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
     return hipLaunchCooperativeKernel((const void *)score_mfma_cluster_kernel<G, NW>, dim3(pl.nb), dim3(NW * 64),
                                       args, (unsigned)lds, st);
+}
+
+// Geometry of the staged cluster path (raw scores of at most kStageLds bytes per block); false
+// when it does not apply.
+template <int G>
+static bool stage_plan(int N, ClusterPlan &pl)
+{
+    constexpr int NW = kClusterWaves;
+    constexpr int GP = (G + 1) & ~1;
+    int dev = 0, n_cu = 0, coop = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
+        return false;
+    if (!coop || n_cu <= 0) return false;
+    if (allow_dynamic_lds((const void *)score_mfma_stage_kernel<G>, kStageLds) != hipSuccess) return false;
+    const int kmax = (kStageLds / (GP * 4)) & ~15;
+    int Ps = 1;
+    while ((long long)Ps * kmax < N) Ps *= 2;
+    if (Ps > 32) return false;
+    const int Kb = ((N + Ps - 1) / Ps + 15) & ~15;
+    const int nb = (n_cu / (8 * Ps)) * 8 * Ps;
+    if (nb <= 0 || nb > kClusterMaxBlocks) return false;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_stage_kernel<G>, NW * 64,
+                                                     (size_t)Kb * GP * 4) != hipSuccess || per_cu < 1)
+        return false;
+    pl.Ps = Ps;
+    pl.Kb = Kb;
+    pl.nb = nb;
+    pl.cpx = nb / 8 / Ps;
+    pl.C = nb / Ps;
+    return true;
+}
+
+template <int G>
+static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u32x4 *ops, const float *pivot,
+                                 int N, int streams, float *F, float *raw_out, float *stats,
+                                 const tria_score_ws &lay, char *ws, hipStream_t st)
+{
+    constexpr int NW = kClusterWaves;
+    constexpr int GP = (G + 1) & ~1;
+    const size_t lds = (size_t)pl.Kb * GP * 4;
+    uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);
+    fill_u32_kernel<<<(pl.C + 255) / 256, 256, 0, st>>>(arrive, pl.C, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    double *xpart = (double *)(ws + lay.xpart_off);
+    int *err = (int *)(ws + lay.err_off);
+    int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
+    void *args[] = {(void *)&kp, (void *)&ops, (void *)&pivot, &n, &S, &Ps, &Kb, &cpx, &C,
+                    (void *)&xpart, (void *)&arrive, (void *)&F, (void *)&raw_out, (void *)&stats, (void *)&err};
+    KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
+    return hipLaunchCooperativeKernel((const void *)score_mfma_stage_kernel<G>, dim3(pl.nb), dim3(NW * 64), args,
+                                      (unsigned)lds, st);
 }
 
 // ---- maximum over the future offsets (TRIA_OFFSET_MAX) ------------------------------------------
@@ -1210,6 +1537,8 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
         return hipGetLastError();
     }
     ClusterPlan pl;
+    if (cluster_enabled() && stage_plan<G>(N, pl))
+        return launch_stage_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
     if (cluster_enabled() && cluster_plan<G>(N, pl))
         return launch_cluster_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
     // raw scores go straight into the caller's raw output when there is one (same layout)
