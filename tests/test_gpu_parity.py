@@ -59,19 +59,29 @@ def test_tiled_path_ragged_tail(orc, T, path, G, dtype, N):
 
 def test_tiled_path_long_stream(orc, T, path):
     """A stream of 70001 keys: 69 tiles of 1024 keys, the last one ragged (369 keys); on the
-    cluster path (G = 2) 8 blocks of 8752 keys, the last one with 8737."""
+    staged cluster path (G = 2) 16 blocks of 4384 keys, the last one with 4241."""
     cfg = variant(2, name=f"tiled-long-{path}", n_q_heads=2, n_kv_heads=1, n_seq=1, n_keys=70001, budget=7000,
                   t_fixed=90000, calib="head_r", r_range=(0.6, 0.99), seed=210)
     run_case(orc, T, cfg)
 
 
 def test_cluster_path_many_rounds(orc, T, path):
-    """480 streams of 3000 keys with G = 8: one block per stream (128 KB of raw scores fit), 256
-    clusters per grid, so part of the grid runs a second round; sampled streams on both sides
-    of the round boundary."""
+    """480 streams of 3000 keys with G = 8: on the staged cluster path two blocks per stream
+    (1504 and 1496 keys), 128 clusters per grid, so streams run up to four rounds; sampled
+    streams on both sides of every round boundary."""
     cfg = variant(2, name=f"rounds-{path}", n_q_heads=64, n_kv_heads=8, n_seq=1, n_layers=60, n_keys=3000,
                   budget=900, t_fixed=4000, calib="head_r", r_range=(0.6, 0.99), seed=212)
-    run_case(orc, T, cfg, sample=np.array([0, 1, 200, 255, 256, 257, 479]))
+    run_case(orc, T, cfg, sample=np.array([0, 1, 127, 128, 255, 256, 383, 384, 479]))
+
+
+@pytest.mark.parametrize("N", [65536, 100001])
+def test_widest_clusters(orc, T, N):
+    """G = 8: 65536 keys fill the staged path's widest cluster (32 blocks of 2048 keys); 100001
+    keys are past its reach and run on the register-ring cluster path (32 blocks of 3136 keys,
+    the last one with 2785)."""
+    cfg = variant(2, name=f"g8-N{N}", n_q_heads=8, n_kv_heads=1, n_seq=2, n_keys=N, budget=N // 11,
+                  t_fixed=N + 5000, calib="head_r", r_range=(0.6, 0.99), seed=214)
+    run_case(orc, T, cfg)
 
 
 def test_stream_beyond_cluster_reach(orc, T):

@@ -1,9 +1,10 @@
 """Top-B selection on the GPU against the oracle's full sort, on hand-made score rows.
 
-The LDS selection brackets the threshold from a strided sample of the keys and falls back to a
+The selection brackets the threshold from a strided sample of the scores and falls back to a
 radix selection over all keys when the bracket misses; these rows exercise both routes (sample
-ranges that miss, heavy ties, a sampled outlier, constant rows), both block sizes (short and
-long streams), the global kernel past the LDS limit, and the edges of B.  Every result is
+ranges that miss, heavy ties, a sampled outlier, constant rows) in both bracketed kernels (the
+one that streams F for 8193-32768 keys, the one that copies short streams to LDS), the global
+kernel past 32768 keys, and the edges of B.  Every result is
 compared bit-exactly with the oracle's selection on the same float32 scores (ties to the lower
 index, output ascending).
 """
