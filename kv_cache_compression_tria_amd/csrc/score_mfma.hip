@@ -839,13 +839,15 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
 // load instruction covers 1 KB of consecutive key bytes (four whole rows), which streams from HBM
 // faster than the matrix-core operand layout does, and the operands are then read from LDS.  Chunk
 // c of row r of a tile sits at slot 16 r + (c ^ r), so the operand reads (row j, chunk
-// 4 kb + g for lane (g, j)) hit distinct bank groups.  Each wave owns two 4 KB slots: the tile of
-// item i + 1 is in flight while item i is scored.  The compiler does not see these loads, so the
-// kernel waits for them itself (vmcnt counts them in issue order) and issues no other wave-local
-// vector-memory load between a tile's load and its wait except where it waits for everything.
-// The raw scores of a round take at most 64 KB of LDS (2048 keys at G = 8), so a stream of 32768
-// keys spans a cluster of 16 blocks.  The arrival of a round is counted after the next round's
-// first ring wait, which covers the partial sums' stores, instead of draining the loads in flight.
+// 4 kb + g for lane (g, j)) hit distinct bank groups.  Each wave owns two 4 KB slots: item i's
+// tile is read out of its slot into registers first, and the slot is then refilled with the tile
+// of item i + 2, so the tiles of items i + 1 and i + 2 are in flight while item i is scored.  The
+// compiler does not see these loads, so the kernel waits for them itself (vmcnt counts vector
+// memory operations in issue order; other operations issued after a tile only make a wait
+// stricter).  The raw scores of a round take at most 64 KB of LDS (2048 keys at G = 8), so a
+// stream of 32768 keys spans a cluster of 16 blocks.  The arrival of a round is counted after the
+// next round's second ring wait, which covers the partial sums' stores, instead of draining the
+// loads in flight.
 constexpr int kStageLds = 64 * 1024;   // raw scores of one block's part of a stream
 constexpr int kStageDefer = 16;        // items scored before the previous round is finished
 
@@ -915,8 +917,20 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             dma16(base + (row < valid ? row : 0) * 16 + ((lane & 15) ^ row), slot + 64 * m);
         }
     };
-    // wait until every memory-to-LDS load but the newest tile's (4 instructions) has landed
+    // wait until every vector memory operation but the newest 4 (the newest tile's loads, when
+    // nothing else followed them) has completed
     auto wait_ring = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
+    // the operand words (1 KB per wave) and pivots of stream sn, loaded into LDS
+    auto stage_ops = [&](int sn) {
+        dma16(ops + (size_t)sn * kOps * 64 + wid * 64 + lane, &ops_l[wid * 64]);
+        if (wid == 0 && lane < G) {
+            const uint32_t la = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)piv_l);
+            const float *src = pivot + (size_t)sn * G + lane;   // lane l -> piv_l[l]
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la)
+                         : "memory", "m0");
+        }
+    };
     auto read_item = [&](int i, u32x4 (&b)[4]) {
         const u32x4 *slot = &stg[wid][i & 1][0];
 #pragma unroll
@@ -929,12 +943,16 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
         }
     };
-    // score item i (item li of its round) into v: its tile was loaded one item earlier
-    auto score_item = [&](int i, int li, float (&v)[2]) {
-        load_item(i + 1);
+    // score item i (item li of its round) into v: its tile was loaded two items earlier; once it
+    // is in registers its slot takes item i + 2's tile (after the operands of stream sn_ops, if
+    // sn_ops >= 0, so that the next ring wait covers them)
+    auto score_item = [&](int i, int li, int sn_ops, float (&v)[2]) {
         wait_ring();
         u32x4 b[4];
         read_item(i, b);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot has been read
+        if (sn_ops >= 0) stage_ops(sn_ops);
+        load_item(i + 2);
         ws.score(b, nkeys - (wid + NW * li) * 16, v);
     };
     // round r's partial sums: wave 0 stores its block's per-head sums as agent-scope atomics; the
@@ -1048,24 +1066,29 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     };
 
     load_item(0);
+    load_item(1);
+    const int ops_li = max(nt - 2, 0);   // the item that loads the next stream's operands
     for (int r = 0; r < rounds; ++r) {
+        const bool more = r + 1 < rounds;
+        const int sn = more ? cl + (r + 1) * C : -1;
         int li = 0;
         if (r > 0) {
             // The first items of a round keep their scores in registers while the previous round
             // is finished (its wait for the slowest block is covered by scoring).  The round's
-            // last item always runs below, where it brings in the next stream's operands.  The
-            // previous round's arrival is counted after the first item's ring wait, which covers
-            // the partial sums' stores; without such an item, after waiting for everything.
+            // last item always runs below.  The previous round's arrival is counted after the
+            // second item's ring wait, the first one that every operation issued before the
+            // previous round's partial-sum stores precedes; without such an item, after waiting
+            // for everything.
             const int nd = min(kStageDefer, nt - 1);
             float dv[kStageDefer][2];
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q) {
                 if (q < nd) {
-                    score_item(r * nt + q, q, dv[q]);
-                    if (q == 0) count_arrival();
+                    score_item(r * nt + q, q, q == ops_li ? sn : -1, dv[q]);
+                    if (q == 1) count_arrival();
                 }
             }
-            if (nd == 0) {
+            if (nd < 2) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 count_arrival();
             }
@@ -1075,26 +1098,13 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
                 if (q < nd) put(q, dv[q]);
             li = nd;
         }
-        const bool more = r + 1 < rounds;
         for (; li < nt; ++li) {
-            if (li == nt - 1 && more) {
-                // the next stream's operand words (1 KB per wave) and pivots, loaded into LDS
-                // ahead of this item's tile, so that this item's ring wait covers them
-                const int sn = cl + (r + 1) * C;
-                dma16(ops + (size_t)sn * kOps * 64 + wid * 64 + lane, &ops_l[wid * 64]);
-                if (wid == 0 && lane < G) {
-                    const uint32_t la = __builtin_amdgcn_readfirstlane(
-                        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)piv_l);
-                    const float *src = pivot + (size_t)sn * G + lane;   // lane l -> piv_l[l]
-                    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la)
-                                 : "memory", "m0");
-                }
-            }
             float v[2];
-            score_item(r * nt + li, li, v);
+            score_item(r * nt + li, li, li == ops_li ? sn : -1, v);
             put(li, v);
         }
         // ---- end of round r: stage and publish the partial sums, switch to the next stream
+        if (more && nt < 2) wait_ring();   // the operands loaded by the round's only item
         block_sums_stage(bs, ws.m);
         __syncthreads();
         publish(r);
