@@ -860,7 +860,18 @@ __device__ __forceinline__ void dma16(const u32x4 *src, const u32x4 *lds_base)
                  : "memory", "m0");
 }
 
+// Items per wave and round of a block that holds kStageLds bytes of raw scores (a full block).
 template <int G>
+constexpr int stage_full_items()
+{
+    constexpr int GP = (G + 1) & ~1;
+    constexpr int kmax = (kStageLds / (GP * 4)) & ~15;
+    return ((kmax + 15) / 16 + kClusterWaves - 1) / kClusterWaves;
+}
+
+// NTC > 0: every block of the launch runs exactly NTC items per wave and round (known at compile
+// time, so that the item and round indices are shifts and masks, not divisions); 0: any count.
+template <int G, int NTC>
 __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
     int streams, int Ps, int Kb, int cpx, int C, double *__restrict__ xpart, uint32_t *__restrict__ arrive,
@@ -886,7 +897,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     const int j0 = part * Kb;
     const int nkeys = max(0, min(Kb, N - j0));
     const int ntiles16 = (nkeys + 15) >> 4;
-    const int nt = max(1, (ntiles16 + NW - 1) / NW);   // items per wave and round
+    const int nt = NTC > 0 ? NTC : max(1, (ntiles16 + NW - 1) / NW);   // items per wave and round
     const int total = rounds * nt;
 
     WaveScorer<G> ws;
@@ -917,19 +928,33 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             dma16(base + (row < valid ? row : 0) * 16 + ((lane & 15) ^ row), slot + 64 * m);
         }
     };
-    // wait until every vector memory operation but the newest 4 (the newest tile's loads, when
-    // nothing else followed them) has completed
-    auto wait_ring = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
-    // the operand words (1 KB per wave) and pivots of stream sn, loaded into LDS
-    auto stage_ops = [&](int sn) {
+    // Wait until every vector memory operation but the newest 4 + e has completed: the newest
+    // tile's 4 loads and the e operations (all written out in this kernel, so their count is
+    // exact) that followed them.  Operations complete in issue order for this count, so a load
+    // or store issued just after a tile is next waited for together with the following tile.
+    auto wait_ring = [&](int e) {
+        switch (e) {
+        case 0: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        }
+    };
+    // the operand words (1 KB per wave) and pivots of stream sn, loaded into LDS; returns the
+    // number of load instructions issued
+    auto stage_ops = [&](int sn) -> int {
         dma16(ops + (size_t)sn * kOps * 64 + wid * 64 + lane, &ops_l[wid * 64]);
-        if (wid == 0 && lane < G) {
+        if (wid != 0) return 1;
+        if (lane < G) {
             const uint32_t la = __builtin_amdgcn_readfirstlane(
                 (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)piv_l);
             const float *src = pivot + (size_t)sn * G + lane;   // lane l -> piv_l[l]
             asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la)
                          : "memory", "m0");
         }
+        return 2;
     };
     auto read_item = [&](int i, u32x4 (&b)[4]) {
         const u32x4 *slot = &stg[wid][i & 1][0];
@@ -943,34 +968,46 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
         }
     };
-    // score item i (item li of its round) into v: its tile was loaded two items earlier; once it
-    // is in registers its slot takes item i + 2's tile (after the operands of stream sn_ops, if
-    // sn_ops >= 0, so that the next ring wait covers them)
-    auto score_item = [&](int i, int li, int sn_ops, float (&v)[2]) {
-        wait_ring();
-        u32x4 b[4];
-        read_item(i, b);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot has been read
-        if (sn_ops >= 0) stage_ops(sn_ops);
-        load_item(i + 2);
-        ws.score(b, nkeys - (wid + NW * li) * 16, v);
-    };
-    // round r's partial sums: wave 0 stores its block's per-head sums as agent-scope atomics; the
-    // arrival is counted by count_arrival once a ring wait has covered the stores
-    auto publish = [&](int r) {
-        if (wid != 0) return;
+    // round r's partial sums (staged in bs): wave 0 stores its block's per-head sums (s1, s2, min,
+    // max as four doubles, two 16-byte stores); the arrival is counted by count_arrival once a
+    // ring wait has covered the stores.  Both return the number of instructions issued.
+    auto publish = [&](int r) -> int {
+        if (wid != 0) return 0;
         double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
         if (lane < G) {
             const Sums t2 = block_sums_of(bs, lane);
             double *q = xr + ((size_t)part * G + lane) * 4;
-            __hip_atomic_store(q + 0, t2.s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(q + 1, t2.s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(q + 2, (double)t2.mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(q + 3, (double)t2.mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const u32x4 w0 = __builtin_bit_cast(u32x4, double2{t2.s1, t2.s2});
+            const u32x4 w1 = __builtin_bit_cast(u32x4, double2{(double)t2.mn, (double)t2.mx});
+            // (a store of more than 8 bytes reads its data after issue: one wait state before
+            // the registers may be rewritten)
+            asm volatile("global_store_dwordx4 %0, %1, off\n\tglobal_store_dwordx4 %0, %2, off offset:16\n\ts_nop 1"
+                         ::"v"(q), "v"(w0), "v"(w1) : "memory");
         }
+        return 2;
     };
-    auto count_arrival = [&]() {
-        if (wid == 0 && lane == 0) __hip_atomic_fetch_add(&arrive[cl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    auto count_arrival = [&]() -> int {
+        if (wid != 0) return 0;
+        if (lane == 0)
+            asm volatile("global_atomic_add %0, %1, off" ::"v"(&arrive[cl]), "v"(1u) : "memory");
+        return 1;
+    };
+    // score item i (item li of its round) into v: its tile was loaded two items earlier and e_prev
+    // operations followed the newest tile.  Once the tile is in registers its slot takes item
+    // i + 2's tile, followed by the operands of stream sn_ops (sn_ops >= 0), round pub_r's partial
+    // sums (pub_r >= 0) and the arrival (cnt).  Returns the number of those operations.
+    auto score_item = [&](int i, int li, int e_prev, int sn_ops, int pub_r, bool cnt, float (&v)[2]) -> int {
+        wait_ring(e_prev);
+        u32x4 b[4];
+        read_item(i, b);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot has been read
+        load_item(i + 2);
+        int e = 0;
+        if (sn_ops >= 0) e += stage_ops(sn_ops);
+        if (pub_r >= 0) e += publish(pub_r);
+        if (cnt) e += count_arrival();
+        ws.score(b, nkeys - (wid + NW * li) * 16, v);
+        return e;
     };
     auto finish = [&](int r) {
         const int sid = cl + r * C;
@@ -1067,7 +1104,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 
     load_item(0);
     load_item(1);
-    const int ops_li = max(nt - 2, 0);   // the item that loads the next stream's operands
+    const int ops_li = max(nt - 3, 0);   // the item that loads the next stream's operands
+    int e = 0;                           // operations issued after the newest tile
     for (int r = 0; r < rounds; ++r) {
         const bool more = r + 1 < rounds;
         const int sn = more ? cl + (r + 1) * C : -1;
@@ -1075,24 +1113,22 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         if (r > 0) {
             // The first items of a round keep their scores in registers while the previous round
             // is finished (its wait for the slowest block is covered by scoring).  The round's
-            // last item always runs below.  The previous round's arrival is counted after the
-            // second item's ring wait, the first one that every operation issued before the
-            // previous round's partial-sum stores precedes; without such an item, after waiting
-            // for everything.
+            // last item always runs below.  The previous round's partial sums are stored after
+            // the first item's tile load, and the arrival is counted at the third item, whose
+            // ring wait covers those stores; with fewer items, after waiting for everything.
             const int nd = min(kStageDefer, nt - 1);
             float dv[kStageDefer][2];
 #pragma unroll
-            for (int q = 0; q < kStageDefer; ++q) {
-                if (q < nd) {
-                    score_item(r * nt + q, q, q == ops_li ? sn : -1, dv[q]);
-                    if (q == 1) count_arrival();
-                }
-            }
-            if (nd < 2) {
+            for (int q = 0; q < kStageDefer; ++q)
+                if (q < nd)
+                    e = score_item(r * nt + q, q, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1, q == 2, dv[q]);
+            if (nd < 3) {
+                if (nd == 0) publish(r - 1);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 count_arrival();
             }
             finish(r - 1);
+            e = 0;                       // the finish's stores only make the next wait stricter
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
                 if (q < nd) put(q, dv[q]);
@@ -1100,16 +1136,19 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
         for (; li < nt; ++li) {
             float v[2];
-            score_item(r * nt + li, li, li == ops_li ? sn : -1, v);
+            e = score_item(r * nt + li, li, e, li == ops_li ? sn : -1, -1, false, v);
             put(li, v);
         }
-        // ---- end of round r: stage and publish the partial sums, switch to the next stream
-        if (more && nt < 2) wait_ring();   // the operands loaded by the round's only item
+        // ---- end of round r: stage the partial sums, switch to the next stream
+        if (more && nt < 3) {            // the operands may still be the newest loads
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            e = 0;
+        }
         block_sums_stage(bs, ws.m);
         __syncthreads();
-        publish(r);
         if (more) ws.begin_lds(ops_l, piv_l);
     }
+    publish(rounds - 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last round's stores and tile loads
     count_arrival();
     finish(rounds - 1);
@@ -1198,7 +1237,7 @@ static bool stage_plan(int N, ClusterPlan &pl)
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
         return false;
     if (!coop || n_cu <= 0) return false;
-    if (allow_dynamic_lds((const void *)score_mfma_stage_kernel<G>, kStageLds) != hipSuccess) return false;
+    if (allow_dynamic_lds((const void *)score_mfma_stage_kernel<G, 0>, kStageLds) != hipSuccess) return false;
     const int kmax = (kStageLds / (GP * 4)) & ~15;
     int Ps = 1;
     while ((long long)Ps * kmax < N) Ps *= 2;
@@ -1207,7 +1246,7 @@ static bool stage_plan(int N, ClusterPlan &pl)
     const int nb = (n_cu / (8 * Ps)) * 8 * Ps;
     if (nb <= 0 || nb > kClusterMaxBlocks) return false;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_stage_kernel<G>, NW * 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_stage_kernel<G, 0>, NW * 64,
                                                      (size_t)Kb * GP * 4) != hipSuccess || per_cu < 1)
         return false;
     pl.Ps = Ps;
@@ -1235,9 +1274,15 @@ static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u
     int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
     void *args[] = {(void *)&kp, (void *)&ops, (void *)&pivot, &n, &S, &Ps, &Kb, &cpx, &C,
                     (void *)&xpart, (void *)&arrive, (void *)&F, (void *)&raw_out, (void *)&stats, (void *)&err};
+    // every block full (the first and the last part of a stream run the same item count): the
+    // variant with that count built in
+    auto items = [](int nkeys) { return std::max(1, ((nkeys + 15) / 16 + NW - 1) / NW); };
+    constexpr int full = stage_full_items<G>();
+    const bool exact = items(pl.Kb) == full && items(N - (pl.Ps - 1) * pl.Kb) == full;
+    const void *fn = exact ? (const void *)score_mfma_stage_kernel<G, full> : (const void *)score_mfma_stage_kernel<G, 0>;
+    if (exact && allow_dynamic_lds(fn, kStageLds) != hipSuccess) return hipErrorInvalidValue;
     KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
-    return hipLaunchCooperativeKernel((const void *)score_mfma_stage_kernel<G>, dim3(pl.nb), dim3(NW * 64), args,
-                                      (unsigned)lds, st);
+    return hipLaunchCooperativeKernel(fn, dim3(pl.nb), dim3(NW * 64), args, (unsigned)lds, st);
 }
 
 // ---- maximum over the future offsets (TRIA_OFFSET_MAX) ------------------------------------------
