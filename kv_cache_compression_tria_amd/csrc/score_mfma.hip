@@ -969,8 +969,10 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
     };
     // round r's partial sums (staged in bs): wave 0 stores its block's per-head sums (s1, s2, min,
-    // max as four doubles, two 16-byte stores); the arrival is counted by count_arrival once a
-    // ring wait has covered the stores.  Both return the number of instructions issued.
+    // max as four doubles, two 16-byte stores); the block's arrival flag is set to the number of
+    // rounds it has published once a ring wait has covered those stores.  Both return the number
+    // of instructions issued.  (A flag per block written by a plain store, not a shared counter:
+    // an atomic add held up every later load of the wave by microseconds.)
     auto publish = [&](int r) -> int {
         if (wid != 0) return 0;
         double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
@@ -986,17 +988,18 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
         return 2;
     };
-    auto count_arrival = [&]() -> int {
+    auto count_arrival = [&](int r) -> int {
         if (wid != 0) return 0;
         if (lane == 0)
-            asm volatile("global_atomic_add %0, %1, off" ::"v"(&arrive[cl]), "v"(1u) : "memory");
+            asm volatile("global_store_dword %0, %1, off" ::"v"(&arrive[cl * Ps + part]), "v"((uint32_t)(r + 1))
+                         : "memory");
         return 1;
     };
     // score item i (item li of its round) into v: its tile was loaded two items earlier and e_prev
     // operations followed the newest tile.  Once the tile is in registers its slot takes item
     // i + 2's tile, followed by the operands of stream sn_ops (sn_ops >= 0), round pub_r's partial
-    // sums (pub_r >= 0) and the arrival (cnt).  Returns the number of those operations.
-    auto score_item = [&](int i, int li, int e_prev, int sn_ops, int pub_r, bool cnt, float (&v)[2]) -> int {
+    // sums (pub_r >= 0) and round cnt's arrival (cnt >= 0).  Returns the number of those operations.
+    auto score_item = [&](int i, int li, int e_prev, int sn_ops, int pub_r, int cnt, float (&v)[2]) -> int {
         wait_ring(e_prev);
         u32x4 b[4];
         read_item(i, b);
@@ -1005,7 +1008,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         int e = 0;
         if (sn_ops >= 0) e += stage_ops(sn_ops);
         if (pub_r >= 0) e += publish(pub_r);
-        if (cnt) e += count_arrival();
+        if (cnt >= 0) e += count_arrival(cnt);
         ws.score(b, nkeys - (wid + NW * li) * 16, v);
         return e;
     };
@@ -1013,13 +1016,14 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         const int sid = cl + r * C;
         if (wid == 0) {
             const double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
-            if (lane == 0) {
-                const uint32_t target = (uint32_t)(r + 1) * (uint32_t)Ps;
+            {
+                // lane p < Ps watches part p's flag (the other lanes the last part's)
+                const uint32_t *fl = arrive + (size_t)cl * Ps + min(lane, Ps - 1);
                 unsigned spins = 0;
-                while (__hip_atomic_load(&arrive[cl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                while (!__all(__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(r + 1))) {
                     if (++spins > kSpinLimit ||
                         (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2)) {
-                        atomicOr(err, 2);
+                        if (lane == 0) atomicOr(err, 2);
                         break;
                     }
                     __builtin_amdgcn_s_sleep(2);
@@ -1121,11 +1125,12 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
                 if (q < nd)
-                    e = score_item(r * nt + q, q, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1, q == 2, dv[q]);
+                    e = score_item(r * nt + q, q, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1, q == 2 ? r - 1 : -1,
+                                   dv[q]);
             if (nd < 3) {
                 if (nd == 0) publish(r - 1);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                count_arrival();
+                count_arrival(r - 1);
             }
             finish(r - 1);
             e = 0;                       // the finish's stores only make the next wait stricter
@@ -1136,7 +1141,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
         for (; li < nt; ++li) {
             float v[2];
-            e = score_item(r * nt + li, li, e, li == ops_li ? sn : -1, -1, false, v);
+            e = score_item(r * nt + li, li, e, li == ops_li ? sn : -1, -1, -1, v);
             put(li, v);
         }
         // ---- end of round r: stage the partial sums, switch to the next stream
@@ -1150,7 +1155,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     }
     publish(rounds - 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last round's stores and tile loads
-    count_arrival();
+    count_arrival(rounds - 1);
     finish(rounds - 1);
 }
 
@@ -1266,7 +1271,7 @@ static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u
     constexpr int GP = (G + 1) & ~1;
     const size_t lds = (size_t)pl.Kb * GP * 4;
     uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);
-    fill_u32_kernel<<<(pl.C + 255) / 256, 256, 0, st>>>(arrive, pl.C, 0u);
+    fill_u32_kernel<<<(pl.nb + 255) / 256, 256, 0, st>>>(arrive, pl.nb, 0u);   // one flag per block
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     double *xpart = (double *)(ws + lay.xpart_off);
