@@ -850,6 +850,10 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
 // loads in flight.
 constexpr int kStageLds = 64 * 1024;   // raw scores of one block's part of a stream
 constexpr int kStageDefer = 16;        // items scored before the previous round is finished
+// During the deferred items wave 0 fetches the cluster's arrival flags (item kStageFlags), and, if
+// every block has arrived, its partial sums (item kStageFlags + 2) into LDS, and turns them into
+// the mean and 1/std of every head (item kStageFlags + 4), so that the finish does not wait.
+constexpr int kStageFlags = 6;
 
 // one 16-byte-per-lane memory-to-LDS load: lane l's 16 bytes at `src` land at lds_base + 16 l
 __device__ __forceinline__ void dma16(const u32x4 *src, const u32x4 *lds_base)
@@ -886,6 +890,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     __shared__ __attribute__((aligned(16))) double xs[32 * 8 * 4];   // the cluster's partials of a round
     __shared__ u32x4 ops_l[kOps * 64];             // the next stream's operand words ...
     __shared__ float piv_l[8];                     // ... and pivots, loaded into LDS during a round
+    __shared__ uint32_t flg[64];                   // the cluster's arrival flags, fetched by wave 0
+    __shared__ float pvs[2][8];                    // pivots of the streams of rounds r and r + 1
     static_assert(NW == kOps, "one 1 KB operand load per wave");
     const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
     const int cl = x * cpx + y / Ps, part = y % Ps;
@@ -911,6 +917,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         for (int h = 0; h < 2; ++h) hold(__builtin_bit_cast(uint4, ws.c.an[a][h]));
     hold(__builtin_bit_cast(uint32_t, ws.p[0]));
     hold(__builtin_bit_cast(uint32_t, ws.p[1]));
+    if (wid == 0 && lane < G) pvs[0][lane] = pivot[(size_t)cl * G + lane];
 
     // item i of this wave: tile wid + NW * (i mod nt) of stream cl + (i / nt) C, into slot i & 1;
     // rows at or past the tile's valid count load row 0 (always a real row) and score nothing
@@ -1012,9 +1019,67 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         ws.score(b, nkeys - (wid + NW * li) * 16, v);
         return e;
     };
+    // ---- finishing round r: the cluster's partial sums -> mean and 1/std per head -> F
+    bool early = false;                  // wave 0 fetched round r's partials during the deferred items
+    auto moments = [&](int r) {          // wave 0, from the partials in xs
+        const int sid = cl + r * C;
+        if (lane < G) {
+            const int h = lane;
+            Sums t2;
+            t2.init();
+            for (int pp = 0; pp < Ps; ++pp) {
+                const double *q = xs + ((size_t)pp * G + h) * 4;
+                Sums u;
+                u.s1 = q[0]; u.s2 = q[1]; u.mn = (float)q[2]; u.mx = (float)q[3];
+                t2.add(u);
+            }
+            double mean, sd;
+            finish_moments(t2, (double)pvs[r & 1][h], (double)N, mean, sd);
+            zmu[h] = (float)mean;
+            zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
+            if (part == 0) {
+                if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
+                if (stats) {
+                    stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
+                    stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
+                }
+            }
+        }
+    };
+    // wave 0: the cluster's arrival flags into flg (lane l <- part min(l, Ps - 1)); one load
+    auto fetch_flags = [&]() -> int {
+        if (wid != 0) return 0;
+        const uint32_t *src = arrive + (size_t)cl * Ps + min(lane, Ps - 1);
+        const uint32_t la = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)flg);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc1" ::"v"(src), "s"(la)
+                     : "memory", "m0");
+        return 1;
+    };
+    // wave 0: if every flag in flg shows round r, round r's partials (Ps G x 32 bytes) into xs;
+    // returns the number of loads
+    auto fetch_parts = [&](int r) -> int {
+        if (wid != 0) return 0;
+        early = __all(flg[min(lane, Ps - 1)] >= (uint32_t)(r + 1));
+        if (!early) return 0;
+        const u32x4 *xr = (const u32x4 *)(xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4);
+        const int nch = Ps * G * 2;      // 16-byte chunks, at most 512
+        const int ni = (nch + 63) >> 6;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)xs);
+        for (int m = 0; m < ni; ++m) {
+            const u32x4 *src = xr + min(64 * m + lane, nch - 1);
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(src),
+                         "s"(la + 1024u * (uint32_t)m)
+                         : "memory", "m0");
+        }
+        return ni;
+    };
+    // the block's F of round r: every wave normalises the keys of its own tiles (the rows it will
+    // overwrite with its held scores), so no barrier follows
     auto finish = [&](int r) {
         const int sid = cl + r * C;
-        if (wid == 0) {
+        if (wid == 0 && !early) {
             const double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
             {
                 // lane p < Ps watches part p's flag (the other lanes the last part's)
@@ -1031,30 +1096,26 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             }
             __builtin_amdgcn_wave_barrier();
             // every partial of the round (lane q takes partials q, q + 64, ... of Ps G <= 256; the
-            // rest re-read the last) and the pivots (lanes h < G) in one batch of coherent loads,
-            // waited for once
+            // rest re-read the last) in one batch of coherent loads, waited for once
             const int nq = Ps * G;
             const uint32_t *xq[4];
 #pragma unroll
             for (int it = 0; it < 4; ++it)
                 xq[it] = (const uint32_t *)(xr + (size_t)min(lane + 64 * it, nq - 1) * 4);
-            const float *pv = pivot + (size_t)sid * G + min(lane, G - 1);
             u32x4 w[4][2];
-            float pvv;
             asm volatile(
-                "global_load_dwordx4 %0, %9, off sc1\n\t"
-                "global_load_dwordx4 %1, %9, off offset:16 sc1\n\t"
-                "global_load_dwordx4 %2, %10, off sc1\n\t"
-                "global_load_dwordx4 %3, %10, off offset:16 sc1\n\t"
-                "global_load_dwordx4 %4, %11, off sc1\n\t"
-                "global_load_dwordx4 %5, %11, off offset:16 sc1\n\t"
-                "global_load_dwordx4 %6, %12, off sc1\n\t"
-                "global_load_dwordx4 %7, %12, off offset:16 sc1\n\t"
-                "global_load_dword %8, %13, off\n\t"
+                "global_load_dwordx4 %0, %8, off sc1\n\t"
+                "global_load_dwordx4 %1, %8, off offset:16 sc1\n\t"
+                "global_load_dwordx4 %2, %9, off sc1\n\t"
+                "global_load_dwordx4 %3, %9, off offset:16 sc1\n\t"
+                "global_load_dwordx4 %4, %10, off sc1\n\t"
+                "global_load_dwordx4 %5, %10, off offset:16 sc1\n\t"
+                "global_load_dwordx4 %6, %11, off sc1\n\t"
+                "global_load_dwordx4 %7, %11, off offset:16 sc1\n\t"
                 "s_waitcnt vmcnt(0)"
                 : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[1][0]), "=&v"(w[1][1]), "=&v"(w[2][0]), "=&v"(w[2][1]),
-                  "=&v"(w[3][0]), "=&v"(w[3][1]), "=&v"(pvv)
-                : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(pv)
+                  "=&v"(w[3][0]), "=&v"(w[3][1])
+                : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3])
                 : "memory");
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
@@ -1067,43 +1128,23 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_wave_barrier();
-            if (lane < G) {
-                const int h = lane;
-                Sums t2;
-                t2.init();
-                for (int pp = 0; pp < Ps; ++pp) {
-                    const double *q = xs + ((size_t)pp * G + h) * 4;
-                    Sums u;
-                    u.s1 = q[0]; u.s2 = q[1]; u.mn = (float)q[2]; u.mx = (float)q[3];
-                    t2.add(u);
-                }
-                double mean, sd;
-                finish_moments(t2, (double)pvv, (double)N, mean, sd);
-                zmu[h] = (float)mean;
-                zinv[h] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
-                if (part == 0) {
-                    if (!isfinite(t2.s1) || !isfinite(t2.s2)) atomicOr(err, 1);
-                    if (stats) {
-                        stats[((size_t)sid * G + h) * 2 + 0] = (float)mean;
-                        stats[((size_t)sid * G + h) * 2 + 1] = (float)sd;
-                    }
-                }
-            }
+            moments(r);
         }
-        __syncthreads();
+        early = false;
+        __syncthreads();                 // zmu and zinv
         float *fo = F + (size_t)sid * N + j0;
-        for (int j = threadIdx.x; j < nkeys; j += NW * 64) {
-            float z = -INFINITY;
+        for (int idx = lane; idx < nt * 16; idx += 64) {
+            const int key = (wid + NW * (idx >> 4)) * 16 + (idx & 15);
+            if (key < nkeys) {
+                float z = -INFINITY;
 #pragma unroll
-            for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[j * GP + h] - zmu[h]) * zinv[h]);
-            fo[j] = z;
-        }
-        if (raw_out)
-            for (int q = threadIdx.x; q < G * nkeys; q += NW * 64) {
-                const int h = q / nkeys, j = q - h * nkeys;
-                raw_out[((size_t)sid * G + h) * N + j0 + j] = lraw[j * GP + h];
+                for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[key * GP + h] - zmu[h]) * zinv[h]);
+                fo[key] = z;
+                if (raw_out)
+#pragma unroll
+                    for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + j0 + key] = lraw[key * GP + h];
             }
-        __syncthreads();                           // LDS raw and zmu are reused
+        }
     };
 
     load_item(0);
@@ -1121,12 +1162,19 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             // the first item's tile load, and the arrival is counted at the third item, whose
             // ring wait covers those stores; with fewer items, after waiting for everything.
             const int nd = min(kStageDefer, nt - 1);
+            const bool fetch = nd > kStageFlags + 4;   // room for the early fetch of the partials
             float dv[kStageDefer][2];
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
-                if (q < nd)
+                if (q < nd) {
                     e = score_item(r * nt + q, q, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1, q == 2 ? r - 1 : -1,
                                    dv[q]);
+                    // each step issues its loads after the item's tile; a ring wait two items
+                    // later covers them
+                    if (q == kStageFlags && fetch) e += fetch_flags();
+                    if (q == kStageFlags + 2 && fetch) e += fetch_parts(r - 1);
+                    if (q == kStageFlags + 4 && fetch && wid == 0 && early) moments(r - 1);
+                }
             if (nd < 3) {
                 if (nd == 0) publish(r - 1);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1151,7 +1199,10 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
         block_sums_stage(bs, ws.m);
         __syncthreads();
-        if (more) ws.begin_lds(ops_l, piv_l);
+        if (more) {
+            ws.begin_lds(ops_l, piv_l);
+            if (wid == 0 && lane < G) pvs[(r + 1) & 1][lane] = piv_l[lane];
+        }
     }
     publish(rounds - 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last round's stores and tile loads
