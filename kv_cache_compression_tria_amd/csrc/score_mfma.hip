@@ -892,6 +892,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     __shared__ float piv_l[8];                     // ... and pivots, loaded into LDS during a round
     __shared__ uint32_t flg[64];                   // the cluster's arrival flags, fetched by wave 0
     __shared__ float pvs[2][8];                    // pivots of the streams of rounds r and r + 1
+    __shared__ uint32_t zstamp;                    // rounds whose mean and 1/std are in zmu, zinv
     static_assert(NW == kOps, "one 1 KB operand load per wave");
     const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
     const int cl = x * cpx + y / Ps, part = y % Ps;
@@ -918,14 +919,22 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     hold(__builtin_bit_cast(uint32_t, ws.p[0]));
     hold(__builtin_bit_cast(uint32_t, ws.p[1]));
     if (wid == 0 && lane < G) pvs[0][lane] = pivot[(size_t)cl * G + lane];
+    if (threadIdx.x == 0) zstamp = 0;     // read by the other waves only after the first barrier
 
-    // item i of this wave: tile wid + NW * (i mod nt) of stream cl + (i / nt) C, into slot i & 1;
+    // Item li of a round is tile tile_of(li) of the block's part: wid + NW li, or, when the item
+    // count is a known even number, the pairs 2 NW (li / 2) + 2 wid + (li & 1), so that every
+    // 128-byte line of F (32 keys) belongs to one wave.
+    auto tile_of = [&](int li) {
+        if constexpr (NTC > 0 && NTC % 2 == 0) return 2 * NW * (li >> 1) + 2 * wid + (li & 1);
+        else return wid + NW * li;
+    };
+    // item i of this wave: tile tile_of(i mod nt) of stream cl + (i / nt) C, into slot i & 1;
     // rows at or past the tile's valid count load row 0 (always a real row) and score nothing
     auto load_item = [&](int i) {
         const int ic = min(i, total - 1);
         const int r = ic / nt;
         const int sid = cl + r * C;
-        const int t = min(wid + NW * (ic - r * nt), ntiles16 - 1);
+        const int t = min(tile_of(ic - r * nt), ntiles16 - 1);
         const u32x4 *base = t >= 0 ? k + ((size_t)sid * N + j0 + t * 16) * 16 : k + (size_t)sid * N * 16;
         const int valid = t >= 0 ? nkeys - t * 16 : 0;
         const u32x4 *slot = &stg[wid][i & 1][0];
@@ -969,7 +978,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         for (int kb = 0; kb < 4; ++kb) b[kb] = slot[jj * 16 + ((4 * kb + grp) ^ jj)];
     };
     auto put = [&](int li, const float (&v)[2]) {
-        const int key = (wid + NW * li) * 16 + jj;
+        const int key = tile_of(li) * 16 + jj;
         if (key < nkeys) {
             if (ha < GP) lraw[key * GP + ha] = v[0];
             if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
@@ -1016,7 +1025,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         if (sn_ops >= 0) e += stage_ops(sn_ops);
         if (pub_r >= 0) e += publish(pub_r);
         if (cnt >= 0) e += count_arrival(cnt);
-        ws.score(b, nkeys - (wid + NW * li) * 16, v);
+        ws.score(b, nkeys - tile_of(li) * 16, v);
         return e;
     };
     // ---- finishing round r: the cluster's partial sums -> mean and 1/std per head -> F
@@ -1045,6 +1054,9 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
                 }
             }
         }
+        // the stamp follows the values (a wave's LDS operations complete in order; wait anyway)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) __hip_atomic_store(&zstamp, (uint32_t)(r + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
     // wave 0: the cluster's arrival flags into flg (lane l <- part min(l, Ps - 1)); one load
     auto fetch_flags = [&]() -> int {
@@ -1076,7 +1088,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         return ni;
     };
     // the block's F of round r: every wave normalises the keys of its own tiles (the rows it will
-    // overwrite with its held scores), so no barrier follows
+    // overwrite with its held scores) as soon as wave 0 has stamped the round's mean and 1/std, so
+    // no wave waits for the others
     auto finish = [&](int r) {
         const int sid = cl + r * C;
         if (wid == 0 && !early) {
@@ -1131,15 +1144,18 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             moments(r);
         }
         early = false;
-        __syncthreads();                 // zmu and zinv
+        // wave 0 has stamped round r by now or stamps it without waiting for the other waves
+        while (__hip_atomic_load(&zstamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)(r + 1))
+            __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");   // zmu and zinv are read after the stamp
         float *fo = F + (size_t)sid * N + j0;
         for (int idx = lane; idx < nt * 16; idx += 64) {
-            const int key = (wid + NW * (idx >> 4)) * 16 + (idx & 15);
+            const int key = tile_of(idx >> 4) * 16 + (idx & 15);
             if (key < nkeys) {
                 float z = -INFINITY;
 #pragma unroll
                 for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[key * GP + h] - zmu[h]) * zinv[h]);
-                fo[key] = z;
+                __builtin_nontemporal_store(z, &fo[key]);   // read back by the selection, not now
                 if (raw_out)
 #pragma unroll
                     for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + j0 + key] = lraw[key * GP + h];
