@@ -853,7 +853,7 @@ constexpr int kStageDefer = 16;        // items scored before the previous round
 // During the deferred items wave 0 fetches the cluster's arrival flags (item kStageFlags), and, if
 // every block has arrived, its partial sums (item kStageFlags + 2) into LDS, and turns them into
 // the mean and 1/std of every head (item kStageFlags + 4), so that the finish does not wait.
-constexpr int kStageFlags = 6;
+constexpr int kStageFlags = 10;
 
 // one 16-byte-per-lane memory-to-LDS load: lane l's 16 bytes at `src` land at lds_base + 16 l
 __device__ __forceinline__ void dma16(const u32x4 *src, const u32x4 *lds_base)
@@ -905,6 +905,12 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     const int nkeys = max(0, min(Kb, N - j0));
     const int ntiles16 = (nkeys + 15) >> 4;
     const int nt = NTC > 0 ? NTC : max(1, (ntiles16 + NW - 1) / NW);   // items per wave and round
+    // When every part runs the same item count, block `part` scores part (part + r) mod Ps of its
+    // round-r stream, so that a part that streams slower is not always the same block's (every
+    // block waits for its cluster's slowest each round); partial sums are filed by part, so the
+    // merge order and the results do not change.
+    auto prt = [&](int r) { return NTC > 0 ? ((part + r) & (Ps - 1)) : part; };
+    auto nk_of = [&](int r) { return max(0, min(Kb, N - prt(r) * Kb)); };
     const int total = rounds * nt;
 
     WaveScorer<G> ws;
@@ -934,9 +940,10 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         const int ic = min(i, total - 1);
         const int r = ic / nt;
         const int sid = cl + r * C;
-        const int t = min(tile_of(ic - r * nt), ntiles16 - 1);
-        const u32x4 *base = t >= 0 ? k + ((size_t)sid * N + j0 + t * 16) * 16 : k + (size_t)sid * N * 16;
-        const int valid = t >= 0 ? nkeys - t * 16 : 0;
+        const int nkr = nk_of(r);
+        const int t = min(tile_of(ic - r * nt), ((nkr + 15) >> 4) - 1);
+        const u32x4 *base = t >= 0 ? k + ((size_t)sid * N + prt(r) * Kb + t * 16) * 16 : k + (size_t)sid * N * 16;
+        const int valid = t >= 0 ? nkr - t * 16 : 0;
         const u32x4 *slot = &stg[wid][i & 1][0];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -977,9 +984,9 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) b[kb] = slot[jj * 16 + ((4 * kb + grp) ^ jj)];
     };
-    auto put = [&](int li, const float (&v)[2]) {
+    auto put = [&](int li, int nkr, const float (&v)[2]) {
         const int key = tile_of(li) * 16 + jj;
-        if (key < nkeys) {
+        if (key < nkr) {
             if (ha < GP) lraw[key * GP + ha] = v[0];
             if (ha + 2 < GP) lraw[key * GP + ha + 2] = v[1];
         }
@@ -994,7 +1001,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
         if (lane < G) {
             const Sums t2 = block_sums_of(bs, lane);
-            double *q = xr + ((size_t)part * G + lane) * 4;
+            double *q = xr + ((size_t)prt(r) * G + lane) * 4;
             const u32x4 w0 = __builtin_bit_cast(u32x4, double2{t2.s1, t2.s2});
             const u32x4 w1 = __builtin_bit_cast(u32x4, double2{(double)t2.mn, (double)t2.mx});
             // (a store of more than 8 bytes reads its data after issue: one wait state before
@@ -1015,7 +1022,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     // operations followed the newest tile.  Once the tile is in registers its slot takes item
     // i + 2's tile, followed by the operands of stream sn_ops (sn_ops >= 0), round pub_r's partial
     // sums (pub_r >= 0) and round cnt's arrival (cnt >= 0).  Returns the number of those operations.
-    auto score_item = [&](int i, int li, int e_prev, int sn_ops, int pub_r, int cnt, float (&v)[2]) -> int {
+    auto score_item = [&](int i, int li, int nkr, int e_prev, int sn_ops, int pub_r, int cnt, float (&v)[2]) -> int {
         wait_ring(e_prev);
         u32x4 b[4];
         read_item(i, b);
@@ -1025,7 +1032,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         if (sn_ops >= 0) e += stage_ops(sn_ops);
         if (pub_r >= 0) e += publish(pub_r);
         if (cnt >= 0) e += count_arrival(cnt);
-        ws.score(b, nkeys - tile_of(li) * 16, v);
+        ws.score(b, nkr - tile_of(li) * 16, v);
         return e;
     };
     // ---- finishing round r: the cluster's partial sums -> mean and 1/std per head -> F
@@ -1148,17 +1155,18 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         while (__hip_atomic_load(&zstamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)(r + 1))
             __builtin_amdgcn_s_sleep(1);
         asm volatile("" ::: "memory");   // zmu and zinv are read after the stamp
-        float *fo = F + (size_t)sid * N + j0;
+        const int jr = prt(r) * Kb, nkr = nk_of(r);
+        float *fo = F + (size_t)sid * N + jr;
         for (int idx = lane; idx < nt * 16; idx += 64) {
             const int key = tile_of(idx >> 4) * 16 + (idx & 15);
-            if (key < nkeys) {
+            if (key < nkr) {
                 float z = -INFINITY;
 #pragma unroll
                 for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[key * GP + h] - zmu[h]) * zinv[h]);
                 __builtin_nontemporal_store(z, &fo[key]);   // read back by the selection, not now
                 if (raw_out)
 #pragma unroll
-                    for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + j0 + key] = lraw[key * GP + h];
+                    for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + jr + key] = lraw[key * GP + h];
             }
         }
     };
@@ -1170,6 +1178,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     for (int r = 0; r < rounds; ++r) {
         const bool more = r + 1 < rounds;
         const int sn = more ? cl + (r + 1) * C : -1;
+        const int nkr = nk_of(r);
         int li = 0;
         if (r > 0) {
             // The first items of a round keep their scores in registers while the previous round
@@ -1183,8 +1192,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
                 if (q < nd) {
-                    e = score_item(r * nt + q, q, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1, q == 2 ? r - 1 : -1,
-                                   dv[q]);
+                    e = score_item(r * nt + q, q, nkr, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1,
+                                   q == 2 ? r - 1 : -1, dv[q]);
                     // each step issues its loads after the item's tile; a ring wait two items
                     // later covers them
                     if (q == kStageFlags && fetch) e += fetch_flags();
@@ -1200,13 +1209,13 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             e = 0;                       // the finish's stores only make the next wait stricter
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
-                if (q < nd) put(q, dv[q]);
+                if (q < nd) put(q, nkr, dv[q]);
             li = nd;
         }
         for (; li < nt; ++li) {
             float v[2];
-            e = score_item(r * nt + li, li, e, li == ops_li ? sn : -1, -1, -1, v);
-            put(li, v);
+            e = score_item(r * nt + li, li, nkr, e, li == ops_li ? sn : -1, -1, -1, v);
+            put(li, nkr, v);
         }
         // ---- end of round r: stage the partial sums, switch to the next stream
         if (more && nt < 3) {            // the operands may still be the newest loads

@@ -74,6 +74,15 @@ def test_cluster_path_many_rounds(orc, T, path):
     run_case(orc, T, cfg, sample=np.array([0, 1, 127, 128, 255, 256, 383, 384, 479]))
 
 
+def test_staged_parts_rotate_with_a_ragged_last_part(orc, T):
+    """G = 8 and 32760 keys: 16 blocks of 2048 keys per stream, the last with 2040, all with 16
+    tiles per wave, so blocks take a different part in every round; 40 streams over 16 clusters
+    give two or three rounds.  Sampled streams on both sides of the round boundaries."""
+    cfg = variant(2, name="g8-N32760-rotate", n_q_heads=8, n_kv_heads=1, n_seq=1, n_layers=40, n_keys=32760,
+                  budget=3000, t_fixed=33000, calib="head_r", r_range=(0.6, 0.99), seed=215)
+    run_case(orc, T, cfg, sample=np.array([0, 7, 15, 16, 23, 31, 32, 39]))
+
+
 @pytest.mark.parametrize("N", [65536, 100001])
 def test_widest_clusters(orc, T, N):
     """G = 8: 65536 keys fill the staged path's widest cluster (32 blocks of 2048 keys); 100001
