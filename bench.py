@@ -111,7 +111,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the prune step runs on one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
-              "supported (streams shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+              "supported: this build measures one GPU (streams are independent, so they would shard across GPUs "
+              "with no exchange between them)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -834,20 +834,23 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
 }
 
 // ---- staged cluster path: the keys reach LDS by direct memory-to-LDS loads -------------------
-// The same stream clusters, round protocol and on-chip raw scores as above, with the key tiles
-// fetched by global_load_lds_dwordx4 with the non-temporal hint instead of into registers: each
-// load instruction covers 1 KB of consecutive key bytes (four whole rows), which streams from HBM
+// The same stream clusters and on-chip raw scores as above, with the key tiles fetched by
+// global_load_lds_dwordx4 with the non-temporal hint instead of into registers: each load
+// instruction covers 1 KB of consecutive key bytes (four whole rows), which streams from HBM
 // faster than the matrix-core operand layout does, and the operands are then read from LDS.  Chunk
 // c of row r of a tile sits at slot 16 r + (c ^ r), so the operand reads (row j, chunk
 // 4 kb + g for lane (g, j)) hit distinct bank groups.  Each wave owns two 4 KB slots: item i's
 // tile is read out of its slot into registers first, and the slot is then refilled with the tile
 // of item i + 2, so the tiles of items i + 1 and i + 2 are in flight while item i is scored.  The
-// compiler does not see these loads, so the kernel waits for them itself (vmcnt counts vector
-// memory operations in issue order; other operations issued after a tile only make a wait
-// stricter).  The raw scores of a round take at most 64 KB of LDS (2048 keys at G = 8), so a
-// stream of 32768 keys spans a cluster of 16 blocks.  The arrival of a round is counted after the
-// next round's second ring wait, which covers the partial sums' stores, instead of draining the
-// loads in flight.
+// compiler does not see these loads, so the kernel waits for them itself: vmcnt counts vector
+// memory operations in issue order, every other such operation of the loop is written out and
+// issued right after a tile load, and the next wait leaves exactly those outstanding.  The raw
+// scores of a round take at most 64 KB of LDS (2048 keys at G = 8), so a stream of 32768 keys
+// spans a cluster of 16 blocks.  The exchange of a round: wave 0 stores the block's partial sums
+// after the next round's first tile load and sets the block's arrival flag after the third (a
+// flag per block written by a plain store; an atomic counter completes late and holds up the
+// wave's later waits), fetches the cluster's flags and partials into LDS during the deferred
+// items, and stamps the heads' mean and 1/std in LDS; each wave then writes F for its own keys.
 constexpr int kStageLds = 64 * 1024;   // raw scores of one block's part of a stream
 constexpr int kStageDefer = 16;        // items scored before the previous round is finished
 // During the deferred items wave 0 fetches the cluster's arrival flags (item kStageFlags), and, if
