@@ -995,7 +995,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
     };
     // round r's partial sums (staged in bs): wave 0 stores its block's per-head sums (s1, s2, min,
-    // max as four doubles, two 16-byte stores); the block's arrival flag is set to the number of
+    // max as four doubles, two 16-byte stores, with the cache bits of an agent-scope store, as the
+    // readers load them with those of an agent-scope load); the block's arrival flag is set to the number of
     // rounds it has published once a ring wait has covered those stores.  Both return the number
     // of instructions issued.  (A flag per block written by a plain store, not a shared counter:
     // an atomic add held up every later load of the wave by microseconds.)
@@ -1009,7 +1010,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             const u32x4 w1 = __builtin_bit_cast(u32x4, double2{(double)t2.mn, (double)t2.mx});
             // (a store of more than 8 bytes reads its data after issue: one wait state before
             // the registers may be rewritten)
-            asm volatile("global_store_dwordx4 %0, %1, off\n\tglobal_store_dwordx4 %0, %2, off offset:16\n\ts_nop 1"
+            asm volatile("global_store_dwordx4 %0, %1, off sc1\n\tglobal_store_dwordx4 %0, %2, off offset:16 sc1\n\ts_nop 1"
                          ::"v"(q), "v"(w0), "v"(w1) : "memory");
         }
         return 2;
@@ -1017,7 +1018,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     auto count_arrival = [&](int r) -> int {
         if (wid != 0) return 0;
         if (lane == 0)
-            asm volatile("global_store_dword %0, %1, off" ::"v"(&arrive[cl * Ps + part]), "v"((uint32_t)(r + 1))
+            asm volatile("global_store_dword %0, %1, off sc1" ::"v"(&arrive[cl * Ps + part]), "v"((uint32_t)(r + 1))
                          : "memory");
         return 1;
     };
