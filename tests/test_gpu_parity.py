@@ -83,6 +83,16 @@ def test_staged_parts_rotate_with_a_ragged_last_part(orc, T):
     run_case(orc, T, cfg, sample=np.array([0, 7, 15, 16, 23, 31, 32, 39]))
 
 
+@pytest.mark.parametrize("N", [30000, 32768])
+def test_staged_g4_long_rounds(orc, T, N):
+    """G = 4: 8 blocks per stream.  30000 keys give 30 tiles per wave and round (not every part
+    full: fixed parts); 32768 keys give 32 (every part full: parts rotate).  Both defer 16 tiles
+    and fetch the cluster's partials during them; 40 streams over 32 clusters give two rounds."""
+    cfg = variant(2, name=f"g4-N{N}-rounds", n_q_heads=4, n_kv_heads=1, n_seq=1, n_layers=40, n_keys=N,
+                  budget=N // 10, t_fixed=N + 500, calib="head_r", r_range=(0.6, 0.99), seed=216)
+    run_case(orc, T, cfg, sample=np.array([0, 8, 31, 32, 39]))
+
+
 @pytest.mark.parametrize("N", [65536, 100001])
 def test_widest_clusters(orc, T, N):
     """G = 8: 65536 keys fill the staged path's widest cluster (32 blocks of 2048 keys); 100001
