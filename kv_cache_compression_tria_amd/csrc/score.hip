@@ -43,7 +43,7 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
         w.pivot_off = off;
         off += align256(heads * sizeof(float));
         // partial sums exchanged inside stream clusters (two round slots per block) and the
-        // clusters' arrival counters
+        // clusters' arrival counters (one per cluster) or flags (one per block)
         w.xpart_off = off;
         off += align256((size_t)kClusterMaxBlocks * 2 * TRIA_MAX_G * 4 * sizeof(double));
         w.arrive_off = off;
