@@ -855,8 +855,10 @@ constexpr int kStageLds = 64 * 1024;   // raw scores of one block's part of a st
 constexpr int kStageDefer = 16;        // items scored before the previous round is finished
 // During the deferred items wave 0 fetches the cluster's arrival flags (item kStageFlags), and, if
 // every block has arrived, its partial sums (item kStageFlags + 2) into LDS, and turns them into
-// the mean and 1/std of every head (item kStageFlags + 4), so that the finish does not wait.
-constexpr int kStageFlags = 10;
+// the mean and 1/std of every head (item kStageFlags + 4, or at the finish after a ring wait that
+// the last deferred item's tile load makes exact), so that the finish does not wait for the
+// cluster.
+constexpr int kStageFlags = 11;
 
 // one 16-byte-per-lane memory-to-LDS load: lane l's 16 bytes at `src` land at lds_base + 16 l
 __device__ __forceinline__ void dma16(const u32x4 *src, const u32x4 *lds_base)
@@ -1041,6 +1043,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     };
     // ---- finishing round r: the cluster's partial sums -> mean and 1/std per head -> F
     bool early = false;                  // wave 0 fetched round r's partials during the deferred items
+    bool stamped = false;                // ... and has turned them into mean and 1/std
     auto moments = [&](int r) {          // wave 0, from the partials in xs
         const int sid = cl + r * C;
         if (lane < G) {
@@ -1101,8 +1104,13 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     // the block's F of round r: every wave normalises the keys of its own tiles (the rows it will
     // overwrite with its held scores) as soon as wave 0 has stamped the round's mean and 1/std, so
     // no wave waits for the others
-    auto finish = [&](int r) {
+    // e: operations issued after the newest tile (the partials, if fetched, are older than it)
+    auto finish = [&](int r, int e) {
         const int sid = cl + r * C;
+        if (wid == 0 && early && !stamped) {
+            wait_ring(e);                // the partials have landed
+            moments(r);
+        }
         if (wid == 0 && !early) {
             const double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
             {
@@ -1155,6 +1163,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             moments(r);
         }
         early = false;
+        stamped = false;
         // wave 0 has stamped round r by now or stamps it without waiting for the other waves
         while (__hip_atomic_load(&zstamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)(r + 1))
             __builtin_amdgcn_s_sleep(1);
@@ -1191,7 +1200,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             // the first item's tile load, and the arrival is counted at the third item, whose
             // ring wait covers those stores; with fewer items, after waiting for everything.
             const int nd = min(kStageDefer, nt - 1);
-            const bool fetch = nd > kStageFlags + 4;   // room for the early fetch of the partials
+            // room for the early fetch: the partials' loads must precede the last deferred tile's
+            const bool fetch = nd > kStageFlags + 3;
             float dv[kStageDefer][2];
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
@@ -1202,14 +1212,17 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
                     // later covers them
                     if (q == kStageFlags && fetch) e += fetch_flags();
                     if (q == kStageFlags + 2 && fetch) e += fetch_parts(r - 1);
-                    if (q == kStageFlags + 4 && fetch && wid == 0 && early) moments(r - 1);
+                    if (q == kStageFlags + 4 && fetch && wid == 0 && early) {
+                        moments(r - 1);
+                        stamped = true;
+                    }
                 }
             if (nd < 3) {
                 if (nd == 0) publish(r - 1);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 count_arrival(r - 1);
             }
-            finish(r - 1);
+            finish(r - 1, e);
             e = 0;                       // the finish's stores only make the next wait stricter
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
@@ -1236,7 +1249,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     publish(rounds - 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last round's stores and tile loads
     count_arrival(rounds - 1);
-    finish(rounds - 1);
+    finish(rounds - 1, 0);
 }
 
 __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int n, uint32_t v)
