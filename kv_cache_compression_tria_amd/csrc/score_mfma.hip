@@ -997,11 +997,11 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
     };
     // round r's partial sums (staged in bs): wave 0 stores its block's per-head sums (s1, s2, min,
-    // max as four doubles, two 16-byte stores, with the cache bits of an agent-scope store, as the
-    // readers load them with those of an agent-scope load); the block's arrival flag is set to the number of
-    // rounds it has published once a ring wait has covered those stores.  Both return the number
-    // of instructions issued.  (A flag per block written by a plain store, not a shared counter:
-    // an atomic add held up every later load of the wave by microseconds.)
+    // max as four doubles, two 16-byte stores) and, once a ring wait has covered those stores, sets
+    // the block's arrival flag to the number of rounds it has published.  Both use the cache bits of
+    // an agent-scope store, as the readers load with those of an agent-scope load, and return the
+    // number of instructions issued.  (A flag per block, not a shared counter: an atomic add
+    // completed late and held up every later load wait of the wave.)
     auto publish = [&](int r) -> int {
         if (wid != 0) return 0;
         double *xr = xpart + ((size_t)cl * 2 + (r & 1)) * Ps * G * 4;
