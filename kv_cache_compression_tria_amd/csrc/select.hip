@@ -56,8 +56,9 @@ static_assert(kCand >= kBins0, "the fallback's histogram lives in the candidate 
 static_assert(kSelectBitmapWords >= kBins0, "the LDS selection's fallback histogram lives in the bitmap words");
 static_assert(kSelectShortKeys * 4 + (kSelectBitmapWords + kCand + kSelectDigitBins) * 4 + 1024 <= 64 * 1024,
               "the LDS selection exceeds 64 KB without a dynamic-LDS attribute");
-static_assert((kSelectBitmapWords + 2 * kCand + kSelectDigitBins) * 4 + 1024 <= 64 * 1024,
-              "the streamed selection's static LDS exceeds 64 KB");
+static_assert((kSelectBitmapWords + kCand + kSelectDigitBins) * 4 + kCand * 2 + 1024 <= 34 * 1024,
+              "the streamed selection's LDS no longer lets four blocks share a CU");
+static_assert(kSelectStreamKeys <= 65536, "candidate indices of the streamed selection are 16-bit");
 
 // the score of an order key (inverse of order_key)
 __device__ __forceinline__ float key_float(uint32_t u)
@@ -617,7 +618,8 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     constexpr int SMAX = kSelectSamples;
     constexpr int SPT = (SMAX + NT - 1) / NT;         // samples per thread
     __shared__ uint32_t bm[kSelectBitmapWords];       // the two bitmaps
-    __shared__ uint32_t ckey[kCand], cidx[kCand];     // candidates; the fallback's histogram in ckey
+    __shared__ uint32_t ckey[kCand];                  // candidates' keys; the fallback's histogram
+    __shared__ uint16_t cidx[kCand];                  // candidates' indices (N <= 32768)
     __shared__ uint32_t dh[kSelectDigitBins];
     __shared__ uint32_t scan[NW + 1];
     __shared__ float s_min[NW], s_max[NW];
@@ -791,7 +793,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
                         const uint32_t slot = base + lanes_below(bc[e]);
                         if (slot < (uint32_t)kCand) {
                             ckey[slot] = u[e];
-                            cidx[slot] = (uint32_t)(c0 + 4 * lane + e);
+                            cidx[slot] = (uint16_t)(c0 + 4 * lane + e);
                         }
                     }
                     base += (uint32_t)__builtin_popcountll(bc[e]);
