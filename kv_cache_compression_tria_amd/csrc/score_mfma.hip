@@ -858,7 +858,7 @@ constexpr int kStageDefer = 16;        // items scored before the previous round
 // the mean and 1/std of every head (item kStageFlags + 4, or at the finish after a ring wait that
 // the last deferred item's tile load makes exact), so that the finish does not wait for the
 // cluster.
-constexpr int kStageFlags = 11;
+constexpr int kStageFlags = 12;
 
 // one 16-byte-per-lane memory-to-LDS load: lane l's 16 bytes at `src` land at lds_base + 16 l
 __device__ __forceinline__ void dma16(const u32x4 *src, const u32x4 *lds_base)
@@ -1194,12 +1194,12 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         const int nkr = nk_of(r);
         int li = 0;
         if (r > 0) {
-            // The first items of a round keep their scores in registers while the previous round
-            // is finished (its wait for the slowest block is covered by scoring).  The round's
-            // last item always runs below.  The previous round's partial sums are stored after
+            // The first items of a round (all 16 in a full block) keep their scores in registers
+            // while the previous round is finished (its wait for the slowest block is covered by
+            // scoring).  The previous round's partial sums are stored after
             // the first item's tile load, and the arrival is counted at the third item, whose
             // ring wait covers those stores; with fewer items, after waiting for everything.
-            const int nd = min(kStageDefer, nt - 1);
+            const int nd = min(kStageDefer, nt);
             // room for the early fetch: the partials' loads must precede the last deferred tile's
             const bool fetch = nd > kStageFlags + 3;
             float dv[kStageDefer][2];
