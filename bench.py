@@ -96,6 +96,20 @@ def parse():
 
 
 def cpu_model() -> str:
+    """The host CPU as lscpu reports it (model name, family / model / stepping numbers), else the
+    first model name of /proc/cpuinfo."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = dict(line.split(":", 1) for line in out.splitlines() if ":" in line)
+        f = {a.strip(): b.strip() for a, b in f.items()}
+        name = f.get("Model name", "")
+        if name:
+            return f"{name} (family {f.get('CPU family', '?')}, model {f.get('Model', '?')}, " \
+                   f"stepping {f.get('Stepping', '?')}; {f.get('Socket(s)', '?')} socket(s))"
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
@@ -104,6 +118,33 @@ def cpu_model() -> str:
     except OSError:
         pass
     return platform.processor() or "unknown"
+
+
+def host_info() -> dict:
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu": cpu_model(), "os_cpu_count": os.cpu_count(), "cpus_usable": aff}
+
+
+def copy_bandwidth(torch, dev, nbytes: int = 8 << 30, reps: int = 5) -> float:
+    """Read + write GB/s of a plain device-to-device copy of nbytes (the best of reps), each rep
+    after a cache flush: the achievable streaming rate the kernels are compared with."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(reps):
+        flush.zero_()
+        torch.cuda.synchronize()
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst, flush
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (best * 1e-3) / 1e9
 
 
 def main():
@@ -126,13 +167,14 @@ def main():
         return bench_calib(args, T, torch)
     if args.workload == "decode":
         return bench_decode(args, T, torch, synth)
-    T.set_score_path(T.PATH_TILED if args.score_path == "tiled" else T.PATH_AUTO)
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     t0 = time.time()
     pre_rope = args.variant == "pre_rope"
     flags = {"default": 0, "per_key_phase": T.PER_KEY_PHASE, "pre_rope": T.KEYS_PRE_ROPE,
              "weight_r": T.TRIG_WEIGHT_R, "offset_max": T.OFFSET_MAX}[args.variant]
+    if args.score_path == "tiled":
+        flags |= T.SCORE_TILED
     if args.config >= 4:
         wl = synth.make_device(cfg, dev, pre_rope=pre_rope)
     else:
@@ -149,34 +191,33 @@ def main():
     B = cfg.budget
     n_streams = S * L * Hkv
     calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], Hkv, cfg.theta)
-    ws = T.workspace(T.score_workspace_bytes(calib, S, N, k.dtype), dev)
+    ws = T.workspace(T.prune_workspace_bytes(calib, S, N, B, k.dtype, flags), dev)
     F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device=dev)
     kept = torch.empty((n_streams, min(B, N)), dtype=torch.int32, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    def restore():
-        k.copy_(k0)
-        v.copy_(v0)
-        pos.copy_(pos0)
+    def restore(dst=(k, v, pos), src=(k0, v0, pos0)):
+        for a, b in zip(dst, src):
+            a.copy_(b)
         if not args.no_flush:
             flush.zero_()
 
-    def step():
+    def step(kk=k, vv=v, pp=pos):
         ev[0].record(stream)
         if args.entry == "prune":
-            # the whole step through its own entry point (selection and compaction fused when
-            # the shapes allow)
-            T.prune(calib, k, v, pos, t, B, F=F, kept=kept, flags=flags, ws=ws, stream=stream)
+            # the whole step through its own entry point (score, select and compact on one
+            # stream); the workspace's error word is checked after the timed loop
+            T.prune(calib, kk, vv, pp, t, B, F=F, kept=kept, flags=flags, ws=ws, stream=stream, check=False)
             ev[1].record(stream)
             ev[2].record(stream)
         else:
-            T.score(calib, k, t, F=F, ws=ws, stream=stream, pos=pos if flags & 3 else None, flags=flags)
+            T.score(calib, kk, t, F=F, ws=ws, stream=stream, pos=pp if flags & 3 else None, flags=flags)
             ev[1].record(stream)
             T.select_topB(F, B, kept=kept, stream=stream)
             ev[2].record(stream)
-            T.compact(k, v, pos, kept, B, stream=stream)
+            T.compact(kk, vv, pp, kept, B, stream=stream)
         ev[3].record(stream)
 
     for _ in range(args.warmup):
@@ -200,18 +241,33 @@ def main():
     kern = T.timing_read()
     T.timing_enable(False)
     T.score_check(ws)
+    moved_kept = kept.clone()
+
+    # The same step on the process's first allocation (the generated cache, allocated before
+    # anything else): roles swapped, the timed copy above now serves as the pristine one.
+    restore()
+    torch.cuda.synchronize()
+    first_ms = []
+    for i in range(min(args.steps, 5)):
+        restore((k0, v0, pos0), (k, v, pos))
+        torch.cuda.synchronize()
+        step(k0, v0, pos0)
+        torch.cuda.synchronize()
+        first_ms.append(ev[0].elapsed_time(ev[3]))
+    T.score_check(ws)
+    restore((k0, v0, pos0), (k, v, pos))
+    copy_gbs = copy_bandwidth(torch, dev)
 
     step_ms = phase.sum(axis=1)
     ms = float(step_ms.mean())
     total_keys = n_streams * N
     ar = torch.arange(kept.shape[1], device=dev, dtype=torch.int32)
-    moved = int((kept != ar).sum().item())
+    moved = int((moved_kept != ar).sum().item())
     alg = synth.algorithmic_bytes(cfg, moved)
     r = d * cfg.elem_bytes
     # algorithmic bytes per step of each timed kernel (what the method must move, no overheads);
-    # on the stream-cluster path the scoring kernel also writes F (no separate normaliser).  A
-    # kernel may run as several launches per step (tria_prune selects and compacts the streams in
-    # two halves), so times are summed per step.
+    # on the stream-cluster path the scoring kernel also writes F (no separate normaliser).  Times
+    # are summed per step, so a kernel split over several launches would be counted whole.
     on_chip_finish = kern["normalise"]["launches"] == 0
     kern_bytes = {
         "score_keys": n_streams * N * r + (n_streams * N * 4 if on_chip_finish else 0),   # keys read once (+ F)
@@ -259,12 +315,18 @@ def main():
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernels[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic().get(dom)},
+        "copy_GB_s": round(copy_gbs, 1),
+        "alg_frac_of_copy": round(alg / (ms * 1e-3) / 1e9 / copy_gbs, 4),
+        "placement": {"timed_cache": "allocated after the generated pristine copy (K, V, positions)",
+                      "ms_per_step_first_allocation": round(float(np.mean(first_ms)), 4),
+                      "ms_min_first_allocation": round(float(np.min(first_ms)), 4)},
+        "host": host_info(),
         "wall_s_timed_loop_incl_restore": round(wall_s, 3),
         "gen_s": round(gen_s, 1),
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, pos0, total_keys / (ms * 1e-3), pre_rope,
+        out["cpu_baseline"] = cpu_baseline(args, cfg, wl, k0, v0, pos0, total_keys / (ms * 1e-3), pre_rope,
                                            form="max" if args.variant == "offset_max" else "fac",
                                            weight_r=args.variant == "weight_r")
     calib.free()
@@ -305,7 +367,7 @@ def bench_decode(args, T, torch, synth):
 
     for _ in range(args.warmup):
         pn = step()
-        T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream)
+        T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream, check=False)
     torch.cuda.synchronize()
     T.timing_read()
     T.timing_enable(True)
@@ -315,7 +377,7 @@ def bench_decode(args, T, torch, synth):
             flush.zero_()
         torch.cuda.synchronize()
         ev[0].record(stream)
-        n = T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream)
+        n = T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream, check=False)
         ev[1].record(stream)
         torch.cuda.synchronize()
         assert n == B
@@ -414,24 +476,31 @@ def bench_calib(args, T, torch):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False, form="fac", weight_r=False):
+def cpu_baseline(args, cfg, wl, k0, v0, pos0, gpu_keys_s, pre_rope=False, form="fac", weight_r=False):
     """The fp64 oracle (factored form, OpenMP over streams) on a bounded sample of streams of the
-    same workload, timed on the host cores."""
+    same workload, timed on the host cores: scores, z-score and GQA max, top-B selection, and the
+    oracle's (out-of-place, one stream at a time) compaction of K, V and positions."""
     import synth
     from oracle import oracle
 
     oracle.build()
     N, d = cfg.n_keys, cfg.head_dim
     kk = k0.reshape(-1, N, d)
+    vv = v0.reshape(-1, N, d)
     pp = pos0.reshape(-1, N)
     threads = oracle.max_threads(0)
 
     def run(ids):
         kh = synth.cache_to_host(kk[ids[0]:ids[-1] + 1])
+        vh = synth.cache_to_host(vv[ids[0]:ids[-1] + 1])
         ph = pp[ids[0]:ids[-1] + 1].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.prune_streams(kh, ph, wl["t"], wl["qc"], wl["qn"], wl["rb"], cfg.budget, cfg.n_kv_heads,
-                             stream_ids=ids, form=form, n_threads=threads, pre_rope=pre_rope, weight_r=weight_r)
+        res = oracle.prune_streams(kh, ph, wl["t"], wl["qc"], wl["qn"], wl["rb"], cfg.budget, cfg.n_kv_heads,
+                                   stream_ids=ids, form=form, n_threads=threads, pre_rope=pre_rope,
+                                   weight_r=weight_r)
+        for i in range(len(ids)):
+            for x in (kh, vh, ph):
+                oracle.compact_rows(x[i], res["kept"][i])
         return time.perf_counter() - t0
 
     n = max(1, min(threads, kk.shape[0]))
@@ -444,8 +513,9 @@ def cpu_baseline(args, cfg, wl, k0, pos0, gpu_keys_s, pre_rope=False, form="fac"
             dt = run(np.arange(n))
     keys = n * N
     return {"value": round(keys / dt, 1), "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {kk.shape[0]} streams ({keys} keys), fp64 {form} form, {dt:.1f} s",
-            "cpu": cpu_model(), "gpu_over_cpu": round(gpu_keys_s / (keys / dt), 1)}
+            "sample": f"{n} of {kk.shape[0]} streams ({keys} keys), fp64 {form} form, score + select + "
+                      f"compaction, {dt:.1f} s",
+            "cpu": cpu_model(), "os_cpu_count": os.cpu_count(), "gpu_over_cpu": round(gpu_keys_s / (keys / dt), 1)}
 
 
 if __name__ == "__main__":

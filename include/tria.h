@@ -70,6 +70,14 @@ typedef enum { TRIA_BF16 = 0, TRIA_F32 = 1 } tria_dtype;
                                  norm score; |D| matrix-core contractions per key.  bf16 caches and
                                  at most 32 offsets; combines with TRIA_TRIG_WEIGHT_R, not with the
                                  per-key flags (TRIA_E_UNSUPPORTED). */
+#define TRIA_SCORE_TILED 16u  /* score bf16 streams too long for one block's LDS on the tiled path
+                                 (raw scores through the workspace, separate statistics and z-max
+                                 kernels) instead of the stream clusters (a cooperative grid of one
+                                 block per CU whose blocks keep a stream's raw scores in LDS and
+                                 exchange per-head partial sums).  Same scores within rounding; the
+                                 workspace must then hold the raw scores.  Without this flag the
+                                 clusters are used when the device supports cooperative launch and a
+                                 stream fits 32 blocks, else the tiled path. */
 
 typedef struct tria_calib tria_calib; /* opaque, library-owned, immutable after load */
 
@@ -98,9 +106,14 @@ void tria_free_calib(tria_calib *calib);
 /* Shape queries of a loaded table (return -1 for a NULL handle). */
 int tria_calib_dim(const tria_calib *calib, int which /* 0 L, 1 Hq, 2 Hkv, 3 d, 4 G */);
 
-/* Workspace bytes tria_score needs for n_seq sequences of n_keys keys of the given cache dtype
- * (0 on bad arguments). */
-size_t tria_score_workspace_bytes(const tria_calib *calib, tria_dtype dtype, int n_seq, int n_keys);
+/* Workspace bytes tria_score needs for n_seq sequences of n_keys keys of the given cache dtype with
+ * the given flags (0 on bad arguments).  The size depends on the path the flags and the shapes
+ * select on the calibration table's device: the rotated queries and matrix-core operands always;
+ * the cluster exchange words on the stream-cluster path; raw scores [S][L][Hq][N] fp32 and tile
+ * partials only on the paths that stage raw scores in HBM (fp32 or TRIA_SCORE_TILED streams too
+ * long for one block, TRIA_PER_KEY_PHASE, TRIA_KEYS_PRE_ROPE, TRIA_OFFSET_MAX). */
+size_t tria_score_workspace_bytes(const tria_calib *calib, tria_dtype dtype, int n_seq, int n_keys,
+                                  unsigned flags);
 
 /*
  * Score every key of every stream and write the final score F (steps 1-2 above).
@@ -111,8 +124,8 @@ size_t tria_score_workspace_bytes(const tria_calib *calib, tria_dtype dtype, int
  *   F          device [S][L][Hkv][N] output final scores
  *   raw        device [S][L][Hq][N] optional output of the raw scores S_trig + S_norm (NULL: not written)
  *   head_stats device [S][L][Hq][2] optional output of each head's (mean, population std)
- *   ws         device workspace of at least tria_score_workspace_bytes(), 256-byte aligned;
- *              its contents need not be initialised.
+ *   ws         device workspace of at least tria_score_workspace_bytes(..., flags), 256-byte
+ *              aligned; its contents need not be initialised.
  * Positions and t must satisfy |t - p| < 2^24 and |t + d| < 2^31.
  * A head whose raw scores span at most 2^-16 of their largest magnitude (equal up to rounding)
  * is constant: std 0, and it contributes z = 0.
@@ -148,9 +161,13 @@ tria_status tria_compact(tria_dtype dtype, void *k, void *v, int32_t *pos, const
                          int n_streams, int n_keys, int budget, int head_dim, void *stream);
 
 /* Whole prune step: tria_score, tria_select_topB and tria_compact in sequence on `stream`,
- * with kept written to the caller's buffer.  ws must hold tria_prune_workspace_bytes(). */
+ * with kept written to the caller's buffer.  ws must hold tria_prune_workspace_bytes(..., flags).
+ * The step is asynchronous, so a scoring failure found on the device (a non-finite score, or a
+ * stream cluster's exchange that did not complete) cannot be returned by this call: the selection
+ * then writes kept = 0..min(B,N)-1 and K, V and pos are left untouched.  Confirm the step with
+ * tria_score_check(ws) before relying on the compacted cache. */
 size_t tria_prune_workspace_bytes(const tria_calib *calib, tria_dtype dtype, int n_seq, int n_keys,
-                                  int budget);
+                                  int budget, unsigned flags);
 tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void *v, int32_t *pos,
                        const int32_t *t, int n_seq, int n_keys, int budget, float *F,
                        int32_t *kept, unsigned flags, void *ws, size_t ws_bytes, void *stream);
@@ -177,7 +194,10 @@ const char *tria_status_string(tria_status status);
  * token) so that `budget` rows stay.  *new_len receives the live length afterwards (budget after
  * a prune, else len + n_new).  F [S][L][Hkv][cap] and kept [streams][budget] are scratch outputs
  * of the prune (valid when it ran); ws holds tria_prune_workspace_bytes(calib, dtype, n_seq, cap,
- * budget).  Errors: those of tria_append and tria_prune.
+ * budget, flags).  As with tria_prune, a scoring failure found on the device leaves K, V and pos
+ * as they were (all cap rows live) although *new_len reports budget: confirm the step with
+ * tria_score_check(ws), and on failure keep the live length at cap.
+ * Errors: those of tria_append and tria_prune.
  */
 tria_status tria_append(tria_dtype dtype, void *k, void *v, int32_t *pos, int n_streams, int cap, int len,
                         const void *k_new, const void *v_new, const int32_t *pos_new, int n_new, int head_dim,
@@ -226,18 +246,6 @@ typedef enum {
 tria_status tria_timing_enable(int on);
 tria_status tria_timing_read(double *ms /* [TRIA_TIMER_COUNT] */, int *launches /* [TRIA_TIMER_COUNT] */);
 
-/*
- * Scoring path for bf16 streams too long for one block's LDS (process-wide; for tests and
- * measurement).  TRIA_PATH_AUTO (default): a cooperative grid of one block per CU in which the
- * blocks of a stream cluster keep its raw scores in LDS and exchange per-head partial sums, when
- * the device supports cooperative launch and the stream fits 32 blocks; else the tiled path.
- * TRIA_PATH_TILED: always the tiled path (raw scores through the workspace, separate statistics
- * and z-max kernels).  Both give the same scores within rounding.  Errors: INVALID (unknown path).
- * The cluster path reports a cluster exchange that never completed as TRIA_E_DEVICE from
- * tria_score_check.
- */
-typedef enum { TRIA_PATH_AUTO = 0, TRIA_PATH_TILED = 1 } tria_score_path;
-tria_status tria_set_score_path(int path);
 
 #ifdef __cplusplus
 }

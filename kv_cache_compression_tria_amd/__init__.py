@@ -24,12 +24,13 @@ PER_KEY_PHASE = 1
 KEYS_PRE_ROPE = 2
 TRIG_WEIGHT_R = 4
 OFFSET_MAX = 8
+SCORE_TILED = 16
 
 EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
-    "tria_set_score_path", "tria_calib_stats", "tria_append", "tria_decode_step",
+    "tria_calib_stats", "tria_append", "tria_decode_step",
 )
 TIMERS = ("score_keys", "normalise", "select", "compact", "calib")
 
@@ -63,7 +64,7 @@ def lib() -> ctypes.CDLL:
         L.tria_calib_dim.restype = I
         L.tria_calib_dim.argtypes = [P, I]
         L.tria_score_workspace_bytes.restype = S
-        L.tria_score_workspace_bytes.argtypes = [P, I, I, I]
+        L.tria_score_workspace_bytes.argtypes = [P, I, I, I, U]
         L.tria_score.restype = I
         L.tria_score.argtypes = [P, I, P, P, P, I, I, P, P, P, U, P, S, P]
         L.tria_score_check.restype = I
@@ -75,15 +76,13 @@ def lib() -> ctypes.CDLL:
         L.tria_compact.restype = I
         L.tria_compact.argtypes = [I, P, P, P, P, I, I, I, I, P]
         L.tria_prune_workspace_bytes.restype = S
-        L.tria_prune_workspace_bytes.argtypes = [P, I, I, I, I]
+        L.tria_prune_workspace_bytes.argtypes = [P, I, I, I, I, U]
         L.tria_prune.restype = I
         L.tria_prune.argtypes = [P, I, P, P, P, P, I, I, I, P, P, U, P, S, P]
         L.tria_status_string.restype = ctypes.c_char_p
         L.tria_status_string.argtypes = [I]
         L.tria_timing_enable.restype = I
         L.tria_timing_enable.argtypes = [I]
-        L.tria_set_score_path.restype = I
-        L.tria_set_score_path.argtypes = [I]
         L.tria_calib_stats.restype = I
         L.tria_append.restype = I
         L.tria_append.argtypes = [I, P, P, P, I, I, I, P, P, P, I, I, P]
@@ -193,8 +192,9 @@ def _dtype_arg(dtype) -> int:
     raise TypeError(f"unsupported cache dtype {dtype}")
 
 
-def score_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, dtype=BF16) -> int:
-    return int(lib().tria_score_workspace_bytes(calib.handle, _dtype_arg(dtype), int(n_seq), int(n_keys)))
+def score_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, dtype=BF16, flags: int = 0) -> int:
+    """Workspace bytes of ``score`` with these flags (``tria_score_workspace_bytes``)."""
+    return int(lib().tria_score_workspace_bytes(calib.handle, _dtype_arg(dtype), int(n_seq), int(n_keys), int(flags)))
 
 
 def workspace(nbytes: int, device="cuda"):
@@ -216,7 +216,7 @@ def score(calib: Calib, k, t, F=None, raw=None, head_stats=None, pos=None, flags
     if F is None:
         F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device=k.device)
     if ws is None:
-        ws = workspace(score_workspace_bytes(calib, S, N, k.dtype), k.device)
+        ws = workspace(score_workspace_bytes(calib, S, N, k.dtype, flags), k.device)
     st = lib().tria_score(calib.handle, _dtype_code(k), _ptr(k), _ptr(pos), _ptr(t), S, N, _ptr(F), _ptr(raw),
                           _ptr(head_stats), int(flags), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream))
@@ -257,13 +257,19 @@ def compact(k, v, pos, kept, budget: int, stream=None):
                               d, _stream(stream)), "tria_compact")
 
 
-def prune_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, budget: int, dtype=BF16) -> int:
+def prune_workspace_bytes(calib: Calib, n_seq: int, n_keys: int, budget: int, dtype=BF16, flags: int = 0) -> int:
+    """Workspace bytes of ``prune`` / ``decode_step`` with these flags (``tria_prune_workspace_bytes``)."""
     return int(lib().tria_prune_workspace_bytes(calib.handle, _dtype_arg(dtype), int(n_seq), int(n_keys),
-                                                int(budget)))
+                                                int(budget), int(flags)))
 
 
-def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int = 0, ws=None, stream=None):
-    """Whole prune step (``tria_prune``): returns (F, kept); K, V, pos compacted in place."""
+def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int = 0, ws=None, stream=None,
+          check: bool = True):
+    """Whole prune step (``tria_prune``): returns (F, kept); K, V, pos compacted in place.
+
+    With ``check`` (the default) the call waits for the step and raises if the scoring failed on
+    the device (``tria_score_check``; K, V and pos are then left as they were).  Without it the
+    call stays asynchronous and the caller checks ``ws`` itself."""
     import torch
     S, L, Hkv, N, d = k.shape
     for name, x in (("k", k), ("v", v), ("pos", pos), ("t", t), ("F", F), ("kept", kept)):
@@ -273,11 +279,13 @@ def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int
     if kept is None:
         kept = torch.empty((S * L * Hkv, min(int(budget), N)), dtype=torch.int32, device=k.device)
     if ws is None:
-        ws = workspace(prune_workspace_bytes(calib, S, N, budget, k.dtype), k.device)
+        ws = workspace(prune_workspace_bytes(calib, S, N, budget, k.dtype, flags), k.device)
     st = lib().tria_prune(calib.handle, _dtype_code(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(t), S, N, int(budget),
                           _ptr(F), _ptr(kept), int(flags), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream))
     _check(st, "tria_prune")
+    if check:
+        score_check(ws, stream)
     return F, kept
 
 
@@ -312,9 +320,11 @@ def append(k, v, pos, length: int, k_new, v_new, pos_new, stream=None):
 
 
 def decode_step(calib: Calib, k, v, pos, t, length: int, budget: int, k_new, v_new, pos_new, F=None, kept=None,
-                flags: int = 0, ws=None, stream=None) -> int:
+                flags: int = 0, ws=None, stream=None, check: bool = True) -> int:
     """Append the new rows and, when that fills the cache, prune it back to ``budget`` rows
-    (``tria_decode_step``).  Returns the live length afterwards."""
+    (``tria_decode_step``).  Returns the live length afterwards.  With ``check`` (the default) a
+    step that pruned waits for the device and raises if the scoring failed (the cache is then
+    left unpruned, cap rows live)."""
     import torch
     S, L, Hkv, cap, d = k.shape
     n = k_new.shape[-2]
@@ -326,22 +336,15 @@ def decode_step(calib: Calib, k, v, pos, t, length: int, budget: int, k_new, v_n
     if kept is None:
         kept = torch.empty((S * L * Hkv, min(int(budget), cap)), dtype=torch.int32, device=k.device)
     if ws is None:
-        ws = workspace(prune_workspace_bytes(calib, S, cap, budget, k.dtype), k.device)
+        ws = workspace(prune_workspace_bytes(calib, S, cap, budget, k.dtype, flags), k.device)
     out = ctypes.c_int(0)
     _check(lib().tria_decode_step(calib.handle, _dtype_code(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(t), S, cap,
                                   int(length), int(budget), _ptr(k_new), _ptr(v_new), _ptr(pos_new), n, _ptr(F),
                                   _ptr(kept), int(flags), _ptr(ws), ws.numel() * ws.element_size(),
                                   ctypes.byref(out), _stream(stream)), "tria_decode_step")
+    if check and int(length) + n == cap and cap > int(budget):
+        score_check(ws, stream)
     return out.value
-
-
-PATH_AUTO = 0
-PATH_TILED = 1
-
-
-def set_score_path(path: int):
-    """Choose the long-stream bf16 scoring path (``tria_set_score_path``): PATH_AUTO or PATH_TILED."""
-    _check(lib().tria_set_score_path(int(path)), "tria_set_score_path")
 
 
 def timing_enable(on: bool = True):

@@ -14,6 +14,9 @@
 
 namespace {
 
+constexpr unsigned kScoreFlags =
+    TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE | TRIA_TRIG_WEIGHT_R | TRIA_OFFSET_MAX | TRIA_SCORE_TILED;
+
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // w_f / (2 pi) as an unsigned 64-bit fraction of a turn, i.e. round(w_f / (2 pi) * 2^64).
@@ -31,7 +34,6 @@ uint64_t turn_fraction(double w)
 }  // namespace
 
 namespace tria {
-std::atomic<int> g_score_path{TRIA_PATH_AUTO};
 
 hipError_t allow_dynamic_lds(const void *kernel, int bytes)
 {
@@ -194,10 +196,13 @@ int tria_calib_dim(const tria_calib *c, int which)
     return -1;
 }
 
-size_t tria_score_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys)
+size_t tria_score_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys, unsigned flags)
 {
     if (!c || n_seq <= 0 || n_keys <= 0 || (dt != TRIA_BF16 && dt != TRIA_F32)) return 0;
-    return tria::score_ws_layout(c, dt, n_seq, n_keys).total;
+    if ((flags & ~kScoreFlags) != 0) return 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return 0;   // the path depends on the device
+    return tria::score_ws_layout(c, dt, n_seq, n_keys, flags).total;
 }
 
 tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
@@ -207,8 +212,7 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     if (!c || !k || !t || !F) return TRIA_E_INVALID;
     if (dt != TRIA_BF16 && dt != TRIA_F32) return TRIA_E_INVALID;
     if (n_seq <= 0 || N <= 0 || N > (1 << 24)) return TRIA_E_INVALID;
-    if ((flags & ~(TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE | TRIA_TRIG_WEIGHT_R | TRIA_OFFSET_MAX)) != 0)
-        return TRIA_E_INVALID;
+    if ((flags & ~kScoreFlags) != 0) return TRIA_E_INVALID;
     if ((flags & (TRIA_TRIG_WEIGHT_R | TRIA_OFFSET_MAX)) && (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)))
         return TRIA_E_UNSUPPORTED;
     if ((flags & TRIA_OFFSET_MAX) && (dt != TRIA_BF16 || c->n_off > tria::kMaxdOffsetsLimit)) return TRIA_E_UNSUPPORTED;
@@ -217,16 +221,19 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     if (!aligned(k, 16) || !aligned(F, 4) || (raw && !aligned(raw, 4)) || (stats && !aligned(stats, 4)) ||
         (pos && !aligned(pos, 4)))
         return TRIA_E_INVALID;
-    tria_score_ws lay = tria::score_ws_layout(c, dt, n_seq, N);
-    if (!ws || ws_bytes < lay.total || !aligned(ws, 256)) return TRIA_E_WORKSPACE;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return TRIA_E_INVALID;
+    tria_score_ws lay = tria::score_ws_layout(c, dt, n_seq, N, flags);
+    if (!ws || ws_bytes < lay.total || !aligned(ws, 256)) return TRIA_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     char *w = (char *)ws;
-    float *qrot = (float *)(w + lay.qrot_off);
-    // the rotation kernel also clears the non-finite flag (no memset node: safe under graph capture)
-    if (tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), (flags & TRIA_TRIG_WEIGHT_R) != 0, st) !=
-        hipSuccess)
+    // bf16 keys on the matrix cores rotate the queries in their own prologue kernel; the other paths
+    // get them from the rotation kernel.  Both clear the error word first (no memset node: safe
+    // under graph capture).
+    const bool mfma = dt == TRIA_BF16 && !(flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE));
+    float *qrot = mfma ? nullptr : (float *)(w + lay.qrot_off);
+    if (!mfma && tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), (flags & TRIA_TRIG_WEIGHT_R) != 0,
+                                     st) != hipSuccess)
         return TRIA_E_DEVICE;
     if (tria::launch_score(c, dt, k, pos, t, n_seq, N, qrot, F, raw, stats, flags, lay, w, st) != hipSuccess)
         return TRIA_E_DEVICE;
@@ -260,13 +267,6 @@ tria_status tria_calib_stats(tria_dtype dt, const void *q, int L, int Hq, int n_
     return TRIA_OK;
 }
 
-tria_status tria_set_score_path(int path)
-{
-    if (path != TRIA_PATH_AUTO && path != TRIA_PATH_TILED) return TRIA_E_INVALID;
-    tria::g_score_path.store(path);
-    return TRIA_OK;
-}
-
 size_t tria_select_workspace_bytes(int n_streams, int n_keys, int budget)
 {
     if (n_streams <= 0 || n_keys <= 0 || budget <= 0) return 0;
@@ -279,7 +279,8 @@ tria_status tria_select_topB(const float *F, int n_streams, int N, int B, int32_
     if (!F || !kept || n_streams <= 0 || N <= 0 || B <= 0 || N > (1 << 24)) return TRIA_E_INVALID;
     if (!aligned(F, 4) || !aligned(kept, 4)) return TRIA_E_INVALID;
     if (ws_bytes < tria_select_workspace_bytes(n_streams, N, B) || !ws) return TRIA_E_WORKSPACE;
-    if (tria::launch_select(F, n_streams, N, B, kept, (hipStream_t)stream) != hipSuccess) return TRIA_E_DEVICE;
+    if (tria::launch_select(F, n_streams, N, B, kept, nullptr, (hipStream_t)stream) != hipSuccess)
+        return TRIA_E_DEVICE;
     return TRIA_OK;
 }
 
@@ -297,10 +298,11 @@ tria_status tria_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const in
     return TRIA_OK;
 }
 
-size_t tria_prune_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys, int budget)
+size_t tria_prune_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys, int budget,
+                                  unsigned flags)
 {
     if (!c || n_seq <= 0 || n_keys <= 0 || budget <= 0) return 0;
-    return tria_score_workspace_bytes(c, dt, n_seq, n_keys);
+    return tria_score_workspace_bytes(c, dt, n_seq, n_keys, flags);
 }
 
 tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int32_t *pos,
@@ -311,7 +313,11 @@ tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int
     tria_status s = tria_score(c, dt, k, pos, t, n_seq, N, F, nullptr, nullptr, flags, ws, ws_bytes, stream);
     if (s != TRIA_OK) return s;
     const int n_streams = n_seq * c->L * c->Hkv;
-    if (tria::launch_select(F, n_streams, N, B, kept, (hipStream_t)stream) != hipSuccess) return TRIA_E_DEVICE;
+    // the selection reads the score's error word: after a failed score it keeps every row in place,
+    // so that the compaction moves nothing
+    const int *guard = (const int *)((const char *)ws + tria::score_ws_layout(c, dt, n_seq, N, flags).err_off);
+    if (tria::launch_select(F, n_streams, N, B, kept, guard, (hipStream_t)stream) != hipSuccess)
+        return TRIA_E_DEVICE;
     return tria_compact(dt, k, v, pos, kept, n_streams, N, B, TRIA_D, stream);
 }
 

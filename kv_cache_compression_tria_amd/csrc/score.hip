@@ -23,25 +23,36 @@
 
 namespace tria {
 
-tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int N)
+tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int N, unsigned flags)
 {
     tria_score_ws w{};
     const size_t streams = (size_t)n_seq * c->L * c->Hkv;
     const size_t heads = streams * c->G;
     const size_t fused_lds = (size_t)c->G * (size_t)N * 4 + (size_t)c->G * 192 * 4;
+    const bool perkey = (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0;
+    const bool mfma = dt == TRIA_BF16 && !perkey;          // the matrix-core operand prologue runs
     w.tiled = fused_lds > (size_t)kFusedLdsMax;
     w.tiles = (N + kTileKeys - 1) / kTileKeys;
+    w.cluster = mfma && w.tiled && !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED)) && cluster_path_applies(c->G, N);
+    // raw scores staged in HBM: the per-key and offset-max kernels always, the other long streams
+    // unless a stream cluster keeps them on chip
+    w.has_raw = perkey || (flags & TRIA_OFFSET_MAX) || (w.tiled && !w.cluster);
     size_t off = 0;
     w.err_off = 0;
     off = 256;
-    w.qrot_off = off;
-    off += align256(heads * TRIA_D * sizeof(float));
-    if (dt == TRIA_BF16) {
+    if (!mfma) {
+        // rotated queries of every head (the matrix-core prologue keeps its own in LDS)
+        w.qrot_off = off;
+        off += align256(heads * TRIA_D * sizeof(float));
+    }
+    if (mfma) {
         // matrix-core operands of every stream in lane layout, and the per-head pivots
         w.ops_off = off;
         off += align256(streams * (size_t)mfma_ops_per_stream(c->G) * 64 * 16);
         w.pivot_off = off;
         off += align256(heads * sizeof(float));
+    }
+    if (w.cluster) {
         // partial sums exchanged inside stream clusters (two round slots per block) and the
         // clusters' arrival counters (one per cluster) or flags (one per block)
         w.xpart_off = off;
@@ -49,9 +60,8 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
         w.arrive_off = off;
         off += align256((size_t)kClusterMaxBlocks * sizeof(uint32_t));
     }
-    {
-        // raw scores, tile partials and per-head mean / 1/std: used by the tiled paths and by the
-        // per-key-phase variants at any length (the workspace size does not depend on the flags)
+    if (w.has_raw) {
+        // raw scores [streams][G][N], tile partials and per-head mean / 1/std
         w.raw_off = off;
         off += align256(heads * (size_t)N * sizeof(float));
         w.part_off = off;
@@ -457,6 +467,7 @@ static hipError_t launch_score_t(const tria_calib *c, const void *k, int n_seq, 
             (const uint4 *)k, qrot, c->W, c->L, c->Hkv, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
+    if (!lay.has_raw) return hipErrorInvalidValue;   // the layout did not plan this path
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
     const long long blocks = (long long)streams * lay.tiles;
@@ -497,11 +508,12 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
 {
     if (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE))
         return launch_score_perkey(c, dt, k, pos, t, n_seq, N, flags, F, raw, stats, lay, ws, st);
-    if (flags & TRIA_OFFSET_MAX)
-        return launch_score_maxd(c, k, t, n_seq, N, qrot, (flags & TRIA_TRIG_WEIGHT_R) != 0, F, raw, stats, lay, ws, st);
-    // bf16 caches score on the matrix cores; fp32 caches on the vector ALU
-    return dt == TRIA_BF16 ? launch_score_mfma(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st)
-                           : launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
+    const bool weight_r = (flags & TRIA_TRIG_WEIGHT_R) != 0;
+    if (flags & TRIA_OFFSET_MAX) return launch_score_maxd(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    // bf16 caches score on the matrix cores (their prologue rotates the queries itself); fp32
+    // caches on the vector ALU, with the rotated queries from the workspace
+    if (dt == TRIA_BF16) return launch_score_mfma(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    return launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
 }
 
 }  // namespace tria

@@ -22,13 +22,17 @@
 // pair of accumulator registers brings them together, after which lane (g, j) = (l/16, l%16)
 // owns the finished scores of key j for heads hA(g) = 4(g&1) + (g>>1) and hA(g) + 2.
 //
-// The per-stream A operands are built once per call by prep_operands_kernel in exactly this lane
+// The per-stream A operands are built once per call by prologue_kernel in exactly this lane
 // layout (one coalesced 16-byte load per lane per MFMA in the scoring kernels), together with a
 // per-head pivot P_h (the fp32 score of the stream's first key; any value near the mean would do).
 // Per-head moments are plain fp64 sums of (s - P_h) and (s - P_h)^2, merged by additions in a
 // fixed order at every level (lane -> wave -> block -> stream): deterministic, no divisions, and
 // no cancellation since P_h lies within the spread of the scores.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <utility>
 
 #include "common.cuh"
 #include "tria_internal.h"
@@ -55,30 +59,57 @@ __device__ __forceinline__ float bf16_term(float x, int b)
     return b == 0 ? t0 : (float)(__bf16)(x - t0);
 }
 
-// ---- prologue: per-stream A operands (lane layout) and pivots ----------------------------------
-// grid = streams, block = 64 (one wave).  ops[(sid*kOps + i)*64 + lane]: operand of MFMA i
-// (i < 4: trig K-block i; 4 + 2a + half: norm term a, band half).
+// ---- prologue: rotated queries -> per-stream A operands (lane layout) and pivots -------------
+// One wave per stream (s, l, g).  Lane f rotates band f of the group's G query heads to the
+// sequence's position: Q_f = P_f exp(i w_f t) with the exact turn fraction t w_f / 2pi mod 1
+// (64-bit integer product) and fp64 sin/cos, P_f = qbar_f mean_d exp(i w_f d) from the
+// calibration table, optionally weighted by R_f (the R-weighted form); the G rotated queries stay
+// in LDS.  Each lane then builds its operand words: ops[(sid*kOps + i)*64 + lane] is the operand of
+// MFMA i (i < 4: trig K-block i; 4 + 2a + half: norm term a, band half).  The pivot of head h (the
+// fp32 score of the stream's first key) is a butterfly sum of the lanes' band terms (every lane
+// ends with the same bits).  Block 0 clears the error word and the blocks clear the stream
+// clusters' n_arrive arrival words.
 template <int G>
-__global__ __launch_bounds__(64) void prep_operands_kernel(const u32x4 *__restrict__ k, const float *__restrict__ qrot,
-                                                           const float *__restrict__ W, int L, int Hkv, int N,
-                                                           u32x4 *__restrict__ ops, float *__restrict__ pivot)
+__global__ __launch_bounds__(64) void prologue_kernel(const u32x4 *__restrict__ k, const double2 *__restrict__ P,
+                                                      const uint64_t *__restrict__ nu, const int32_t *__restrict__ t,
+                                                      const float *__restrict__ R, const float *__restrict__ W, int L,
+                                                      int Hkv, int N, u32x4 *__restrict__ ops, float *__restrict__ pivot,
+                                                      int *__restrict__ err, uint32_t *__restrict__ arrive, int n_arrive)
 {
+    __shared__ float q[G][TRIA_D];
     const int sid = blockIdx.x;
     const int lane = threadIdx.x;
     const int g = sid % Hkv;
     const int l = (sid / Hkv) % L;
-    const float *qrow = qrot + (size_t)sid * G * TRIA_D;
-    const float *wrow = W + ((size_t)l * Hkv + g) * G * TRIA_HALF;
+    const int s = sid / (Hkv * L);
+    if (sid == 0 && lane == 0) *err = 0;   // this call's flag (no memset node: safe under graph capture)
+    for (int i = sid * 64 + lane; i < n_arrive; i += gridDim.x * 64) arrive[i] = 0u;
+    const size_t hh0 = ((size_t)l * Hkv + g) * G;   // (layer, first query head of the group)
+    {
+        const int f = lane;
+        const uint64_t turns = (uint64_t)(int64_t)t[s] * nu[f];    // t * w_f / 2pi mod 1, exact
+        double sn, cs;
+        sincospi(2.0 * ((double)(int64_t)turns * 0x1p-64), &sn, &cs);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const double2 pf = P[(hh0 + h) * TRIA_HALF + f];
+            const double wr = R ? (double)R[(hh0 + h) * TRIA_HALF + f] : 1.0;
+            q[h][f] = (float)(wr * (pf.x * cs - pf.y * sn));
+            q[h][TRIA_HALF + f] = (float)(wr * (pf.x * sn + pf.y * cs));
+        }
+    }
+    __syncthreads();
+    const float *wrow = W + hh0 * TRIA_HALF;
     const int j = lane & 15, grp = lane >> 4;
     const int b = j >> 3, h = j & 7;
     const bool live = h < G;
+    const int hq = live ? h : 0;
     u32x4 *o = ops + (size_t)sid * kOps * 64 + lane;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = (__bf16)bf16_term(live ? qrow[h * TRIA_D + 32 * kb + 8 * grp + e] : 0.f, b);
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)bf16_term(live ? q[hq][32 * kb + 8 * grp + e] : 0.f, b);
         o[kb * 64] = __builtin_bit_cast(u32x4, v);
     }
 #pragma unroll
@@ -88,27 +119,31 @@ __global__ __launch_bounds__(64) void prep_operands_kernel(const u32x4 *__restri
             bf16x8 v;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                v[e] = (__bf16)bf16_term((live && a + b < 2) ? wrow[h * TRIA_HALF + 32 * half + 8 * grp + e] : 0.f, b);
+                v[e] = (__bf16)bf16_term((live && a + b < 2) ? wrow[hq * TRIA_HALF + 32 * half + 8 * grp + e] : 0.f, b);
             o[(4 + 2 * a + half) * 64] = __builtin_bit_cast(u32x4, v);
         }
-    if (lane < G) {
-        // pivot: the fp32 score of the stream's first key for head `lane`
-        const uint32_t *row = (const uint32_t *)(k + (size_t)sid * N * 16);
-        const float *q = qrow + lane * TRIA_D;
-        const float *w = wrow + lane * TRIA_HALF;
-        float s = 0.f;
-        for (int f = 0; f < TRIA_HALF; f += 2) {
-            const uint32_t x = row[f / 2], y = row[(TRIA_HALF + f) / 2];
-            const float re0 = bf16_lo(x), re1 = bf16_hi(x), im0 = bf16_lo(y), im1 = bf16_hi(y);
-            s = fmaf(q[f], re0, s);
-            s = fmaf(q[f + 1], re1, s);
-            s = fmaf(q[TRIA_HALF + f], im0, s);
-            s = fmaf(q[TRIA_HALF + f + 1], im1, s);
-            s = fmaf(w[f], sqrtf(re0 * re0 + im0 * im0), s);
-            s = fmaf(w[f + 1], sqrtf(re1 * re1 + im1 * im1), s);
-        }
-        pivot[(size_t)sid * G + lane] = isfinite(s) ? s : 0.f;
+    // pivots: lane f holds band f of the stream's first key
+    const uint16_t *row = (const uint16_t *)(k + (size_t)sid * N * 16);
+    const float re = __uint_as_float((uint32_t)row[lane] << 16), im = __uint_as_float((uint32_t)row[TRIA_HALF + lane] << 16);
+    const float nrm = sqrtf(re * re + im * im);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        float x = fmaf(q[hh][lane], re, fmaf(q[hh][TRIA_HALF + lane], im, wrow[hh * TRIA_HALF + lane] * nrm));
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) x += __shfl_xor(x, o2, 64);
+        if (lane == hh) pivot[(size_t)sid * G + hh] = isfinite(x) ? x : 0.f;
     }
+}
+
+template <int G>
+static hipError_t launch_prologue(const tria_calib *c, const u32x4 *kp, const int32_t *t, int n_seq, int N,
+                                  bool weight_r, u32x4 *ops, float *pivot, int *err, uint32_t *arrive, int n_arrive,
+                                  hipStream_t st)
+{
+    const int streams = n_seq * c->L * c->Hkv;
+    prologue_kernel<G><<<streams, 64, 0, st>>>(kp, c->P, c->nu, t, weight_r ? c->R : nullptr, c->W, c->L, c->Hkv, N,
+                                               ops, pivot, err, arrive, n_arrive);
+    return hipGetLastError();
 }
 
 struct Ops {
@@ -853,11 +888,10 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
 // items, and stamps the heads' mean and 1/std in LDS; each wave then writes F for its own keys.
 constexpr int kStageLds = 64 * 1024;   // raw scores of one block's part of a stream
 constexpr int kStageDefer = 16;        // items scored before the previous round is finished
-// During the deferred items wave 0 fetches the cluster's arrival flags (item kStageFlags), and, if
-// every block has arrived, its partial sums (item kStageFlags + 2) into LDS, and turns them into
-// the mean and 1/std of every head (item kStageFlags + 4, or at the finish after a ring wait that
-// the last deferred item's tile load makes exact), so that the finish does not wait for the
-// cluster.
+// During the deferred items wave 0 fetches the cluster's arrival flags (item kStageFlags) and, if
+// every block has arrived, its partial sums (item kStageFlags + 2) into LDS; at the finish, after a
+// ring wait that the last deferred item's tile load makes exact, it turns them into the mean and
+// 1/std of every head, so that the finish does not wait for the cluster.
 constexpr int kStageFlags = 12;
 
 // one 16-byte-per-lane memory-to-LDS load: lane l's 16 bytes at `src` land at lds_base + 16 l
@@ -893,8 +927,11 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     __shared__ BlockSumsT<NW> bs;
     __shared__ float zmu[8], zinv[8];
     __shared__ __attribute__((aligned(16))) double xs[32 * 8 * 4];   // the cluster's partials of a round
-    __shared__ u32x4 ops_l[kOps * 64];             // the next stream's operand words ...
-    __shared__ float piv_l[8];                     // ... and pivots, loaded into LDS during a round
+    // the next stream's operand words and pivots, loaded into LDS during a round; two buffers by round
+    // parity, so that a round's loads never overwrite what a lagging wave may still read at the
+    // start of the round before (a block barrier separates the two)
+    __shared__ u32x4 ops_l[2][kOps * 64];
+    __shared__ float piv_l[2][8];
     __shared__ uint32_t flg[64];                   // the cluster's arrival flags, fetched by wave 0
     __shared__ float pvs[2][8];                    // pivots of the streams of rounds r and r + 1
     __shared__ uint32_t zstamp;                    // rounds whose mean and 1/std are in zmu, zinv
@@ -970,14 +1007,15 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         default: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
         }
     };
-    // the operand words (1 KB per wave) and pivots of stream sn, loaded into LDS; returns the
-    // number of load instructions issued
-    auto stage_ops = [&](int sn) -> int {
-        dma16(ops + (size_t)sn * kOps * 64 + wid * 64 + lane, &ops_l[wid * 64]);
+    // the operand words (1 KB per wave) and pivots of the stream of round rn, loaded into LDS buffer
+    // rn & 1; returns the number of load instructions issued
+    auto stage_ops = [&](int rn) -> int {
+        const int sn = cl + rn * C;
+        dma16(ops + (size_t)sn * kOps * 64 + wid * 64 + lane, &ops_l[rn & 1][wid * 64]);
         if (wid != 0) return 1;
         if (lane < G) {
             const uint32_t la = __builtin_amdgcn_readfirstlane(
-                (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)piv_l);
+                (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)piv_l[rn & 1]);
             const float *src = pivot + (size_t)sn * G + lane;   // lane l -> piv_l[l]
             asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la)
                          : "memory", "m0");
@@ -1026,16 +1064,16 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     };
     // score item i (item li of its round) into v: its tile was loaded two items earlier and e_prev
     // operations followed the newest tile.  Once the tile is in registers its slot takes item
-    // i + 2's tile, followed by the operands of stream sn_ops (sn_ops >= 0), round pub_r's partial
+    // i + 2's tile, followed by the operands of round rn_ops's stream (rn_ops >= 0), round pub_r's partial
     // sums (pub_r >= 0) and round cnt's arrival (cnt >= 0).  Returns the number of those operations.
-    auto score_item = [&](int i, int li, int nkr, int e_prev, int sn_ops, int pub_r, int cnt, float (&v)[2]) -> int {
+    auto score_item = [&](int i, int li, int nkr, int e_prev, int rn_ops, int pub_r, int cnt, float (&v)[2]) -> int {
         wait_ring(e_prev);
         u32x4 b[4];
         read_item(i, b);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot has been read
         load_item(i + 2);
         int e = 0;
-        if (sn_ops >= 0) e += stage_ops(sn_ops);
+        if (rn_ops >= 0) e += stage_ops(rn_ops);
         if (pub_r >= 0) e += publish(pub_r);
         if (cnt >= 0) e += count_arrival(cnt);
         ws.score(b, nkr - tile_of(li) * 16, v);
@@ -1043,7 +1081,6 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     };
     // ---- finishing round r: the cluster's partial sums -> mean and 1/std per head -> F
     bool early = false;                  // wave 0 fetched round r's partials during the deferred items
-    bool stamped = false;                // ... and has turned them into mean and 1/std
     auto moments = [&](int r) {          // wave 0, from the partials in xs
         const int sid = cl + r * C;
         if (lane < G) {
@@ -1107,7 +1144,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     // e: operations issued after the newest tile (the partials, if fetched, are older than it)
     auto finish = [&](int r, int e) {
         const int sid = cl + r * C;
-        if (wid == 0 && early && !stamped) {
+        if (wid == 0 && early) {
             wait_ring(e);                // the partials have landed
             moments(r);
         }
@@ -1163,7 +1200,6 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             moments(r);
         }
         early = false;
-        stamped = false;
         // wave 0 has stamped round r by now or stamps it without waiting for the other waves
         while (__hip_atomic_load(&zstamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)(r + 1))
             __builtin_amdgcn_s_sleep(1);
@@ -1190,7 +1226,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     int e = 0;                           // operations issued after the newest tile
     for (int r = 0; r < rounds; ++r) {
         const bool more = r + 1 < rounds;
-        const int sn = more ? cl + (r + 1) * C : -1;
+        const int rn = more ? r + 1 : -1;    // the round whose operands this round stages
         const int nkr = nk_of(r);
         int li = 0;
         if (r > 0) {
@@ -1206,16 +1242,12 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 #pragma unroll
             for (int q = 0; q < kStageDefer; ++q)
                 if (q < nd) {
-                    e = score_item(r * nt + q, q, nkr, e, q == ops_li ? sn : -1, q == 0 ? r - 1 : -1,
+                    e = score_item(r * nt + q, q, nkr, e, q == ops_li ? rn : -1, q == 0 ? r - 1 : -1,
                                    q == 2 ? r - 1 : -1, dv[q]);
                     // each step issues its loads after the item's tile; a ring wait two items
                     // later covers them
                     if (q == kStageFlags && fetch) e += fetch_flags();
                     if (q == kStageFlags + 2 && fetch) e += fetch_parts(r - 1);
-                    if (q == kStageFlags + 4 && fetch && wid == 0 && early) {
-                        moments(r - 1);
-                        stamped = true;
-                    }
                 }
             if (nd < 3) {
                 if (nd == 0) publish(r - 1);
@@ -1231,7 +1263,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         }
         for (; li < nt; ++li) {
             float v[2];
-            e = score_item(r * nt + li, li, nkr, e, li == ops_li ? sn : -1, -1, -1, v);
+            e = score_item(r * nt + li, li, nkr, e, li == ops_li ? rn : -1, -1, -1, v);
             put(li, nkr, v);
         }
         // ---- end of round r: stage the partial sums, switch to the next stream
@@ -1242,20 +1274,20 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         block_sums_stage(bs, ws.m);
         __syncthreads();
         if (more) {
-            ws.begin_lds(ops_l, piv_l);
-            if (wid == 0 && lane < G) pvs[(r + 1) & 1][lane] = piv_l[lane];
+            // (two calls with fixed LDS addresses rather than one with a computed one: fewer registers)
+            if ((r + 1) & 1) {
+                ws.begin_lds(ops_l[1], piv_l[1]);
+                if (wid == 0 && lane < G) pvs[1][lane] = piv_l[1][lane];
+            } else {
+                ws.begin_lds(ops_l[0], piv_l[0]);
+                if (wid == 0 && lane < G) pvs[0][lane] = piv_l[0][lane];
+            }
         }
     }
     publish(rounds - 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last round's stores and tile loads
     count_arrival(rounds - 1);
     finish(rounds - 1, 0);
-}
-
-__global__ void fill_u32_kernel(uint32_t *__restrict__ p, int n, uint32_t v)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
 }
 
 // Cluster geometry for a stream of N keys: one block of 8 waves per CU, each keeping the raw
@@ -1307,11 +1339,7 @@ static hipError_t launch_cluster_g(const ClusterPlan &pl, const u32x4 *kp, const
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
     const size_t lds = (size_t)pl.Kb * GP * 4;
-    hipError_t e;
-    uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);
-    fill_u32_kernel<<<(pl.C + 255) / 256, 256, 0, st>>>(arrive, pl.C, 0u);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);   // one counter per cluster, cleared by the prologue
     double *xpart = (double *)(ws + lay.xpart_off);
     int *err = (int *)(ws + lay.err_off);
     int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
@@ -1355,6 +1383,33 @@ static bool stage_plan(int N, ClusterPlan &pl)
     return true;
 }
 
+// The plans above query the device (attributes, occupancy) and raise dynamic-LDS limits: host work
+// of several microseconds that the GPU would otherwise wait for at every call.  Each (device, path,
+// G, N) is planned once and remembered.
+template <int G>
+static bool cached_plan(bool staged, int N, ClusterPlan &pl)
+{
+    static std::mutex mu;
+    static std::map<std::tuple<int, bool, int>, std::pair<bool, ClusterPlan>> memo;   // (device, staged, N)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    const auto key = std::make_tuple(dev, staged, N);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = memo.find(key);
+        if (it != memo.end()) {
+            pl = it->second.second;
+            return it->second.first;
+        }
+    }
+    ClusterPlan p{};
+    const bool ok = staged ? stage_plan<G>(N, p) : cluster_plan<G>(N, p);
+    std::lock_guard<std::mutex> lock(mu);
+    memo[key] = std::make_pair(ok, p);
+    pl = p;
+    return ok;
+}
+
 template <int G>
 static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u32x4 *ops, const float *pivot,
                                  int N, int streams, float *F, float *raw_out, float *stats,
@@ -1363,10 +1418,7 @@ static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
     const size_t lds = (size_t)pl.Kb * GP * 4;
-    uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);
-    fill_u32_kernel<<<(pl.nb + 255) / 256, 256, 0, st>>>(arrive, pl.nb, 0u);   // one flag per block
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);   // one flag per block, cleared by the prologue
     double *xpart = (double *)(ws + lay.xpart_off);
     int *err = (int *)(ws + lay.err_off);
     int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
@@ -1589,18 +1641,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_maxd_kernel(
 
 template <int G>
 static hipError_t launch_maxd_g(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N,
-                                const float *qrot, bool weight_r, float *F, float *raw_out, float *stats,
-                                const tria_score_ws &lay, char *ws, hipStream_t st)
+                                bool weight_r, float *F, float *raw_out, float *stats, const tria_score_ws &lay,
+                                char *ws, hipStream_t st)
 {
     const int streams = n_seq * c->L * c->Hkv;
     const u32x4 *kp = (const u32x4 *)k;
     u32x4 *ops = (u32x4 *)(ws + lay.ops_off);
     float *pivot = (float *)(ws + lay.pivot_off);
-    prep_operands_kernel<G><<<streams, 64, 0, st>>>(kp, qrot, c->W, c->L, c->Hkv, N, ops, pivot);
-    hipError_t e = hipGetLastError();
+    // the norm operands (the trigonometric ones are built per offset by the kernel, R-weighted there)
+    hipError_t e = launch_prologue<G>(c, kp, t, n_seq, N, false, ops, pivot, (int *)(ws + lay.err_off), nullptr, 0, st);
     if (e != hipSuccess) return e;
     e = allow_dynamic_lds((const void *)score_maxd_kernel<G>, kMaxdOffsets * 4 * 64 * 16);
     if (e != hipSuccess) return e;
+    if (!lay.has_raw) return hipErrorInvalidValue;   // the layout did not plan this path
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
     const int chunks = (N + kMaxdKeys - 1) / kMaxdKeys;
@@ -1616,20 +1669,19 @@ static hipError_t launch_maxd_g(const tria_calib *c, const void *k, const int32_
     return launch_tile_finish(G, streams, N, chunks, raw, part, nullptr, F, stats, lay, ws, st);
 }
 
-hipError_t launch_score_maxd(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, const float *qrot,
-                             bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws,
+hipError_t launch_score_maxd(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws,
                              hipStream_t st)
 {
     if (c->n_off > kMaxdOffsets) return hipErrorInvalidValue;
     switch (c->G) {
-    case 1: return launch_maxd_g<1>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 2: return launch_maxd_g<2>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 3: return launch_maxd_g<3>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 4: return launch_maxd_g<4>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 5: return launch_maxd_g<5>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 6: return launch_maxd_g<6>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 7: return launch_maxd_g<7>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
-    case 8: return launch_maxd_g<8>(c, k, t, n_seq, N, qrot, weight_r, F, raw, stats, lay, ws, st);
+    case 1: return launch_maxd_g<1>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 2: return launch_maxd_g<2>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 3: return launch_maxd_g<3>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 4: return launch_maxd_g<4>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 5: return launch_maxd_g<5>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 6: return launch_maxd_g<6>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 7: return launch_maxd_g<7>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 8: return launch_maxd_g<8>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1670,18 +1722,34 @@ hipError_t launch_tile_finish(int G, int streams, int N, int tiles, const float 
 }
 
 template <int G>
-static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
-                                float *raw_out, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+static hipError_t launch_mfma_g(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
+                                float *F, float *raw_out, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
     const int streams = n_seq * c->L * c->Hkv;
     int *err = (int *)(ws + lay.err_off);
     const u32x4 *kp = (const u32x4 *)k;
     u32x4 *ops = (u32x4 *)(ws + lay.ops_off);
     float *pivot = (float *)(ws + lay.pivot_off);
-    prep_operands_kernel<G><<<streams, 64, 0, st>>>(kp, qrot, c->W, c->L, c->Hkv, N, ops, pivot);
-    hipError_t e = hipGetLastError();
+    // the path: one block per stream (on chip), staged or register-ring stream clusters, or tiled
+    enum { kOnChip, kStaged, kRing, kTiled } path = kOnChip;
+    ClusterPlan pl{};
+    if (lay.tiled) {
+        if (lay.cluster) {
+            if (cached_plan<G>(true, N, pl)) path = kStaged;
+            else if (cached_plan<G>(false, N, pl)) path = kRing;
+            else return hipErrorInvalidValue;   // the layout planned a cluster path the device no longer offers
+        } else {
+            if (!lay.has_raw) return hipErrorInvalidValue;
+            path = kTiled;
+        }
+    }
+    // the cluster paths' arrival words (one flag per block, or one counter per cluster) are cleared
+    // by the prologue
+    uint32_t *arrive = (path == kStaged || path == kRing) ? (uint32_t *)(ws + lay.arrive_off) : nullptr;
+    const int n_arrive = path == kStaged ? pl.nb : path == kRing ? pl.C : 0;
+    hipError_t e = launch_prologue<G>(c, kp, t, n_seq, N, weight_r, ops, pivot, err, arrive, n_arrive, st);
     if (e != hipSuccess) return e;
-    if (!lay.tiled) {
+    if (path == kOnChip) {
         const size_t lds = (size_t)G * (N | 1) * 4;
         e = allow_dynamic_lds((const void *)score_mfma_fused_kernel<G>, kFusedLdsMax);
         if (e != hipSuccess) return e;
@@ -1689,11 +1757,8 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
         score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
-    ClusterPlan pl;
-    if (cluster_enabled() && stage_plan<G>(N, pl))
-        return launch_stage_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
-    if (cluster_enabled() && cluster_plan<G>(N, pl))
-        return launch_cluster_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
+    if (path == kStaged) return launch_stage_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
+    if (path == kRing) return launch_cluster_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
     // raw scores go straight into the caller's raw output when there is one (same layout)
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
@@ -1708,18 +1773,40 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, int n_seq, i
     return launch_tile_finish(G, streams, N, lay.tiles, raw, part, pivot, F, stats, lay, ws, st);
 }
 
-hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
-                             float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+template <int G>
+static bool cluster_applies_g(int N)
+{
+    ClusterPlan pl;
+    return cached_plan<G>(true, N, pl) || cached_plan<G>(false, N, pl);
+}
+
+bool cluster_path_applies(int G, int N)
+{
+    switch (G) {
+    case 1: return cluster_applies_g<1>(N);
+    case 2: return cluster_applies_g<2>(N);
+    case 3: return cluster_applies_g<3>(N);
+    case 4: return cluster_applies_g<4>(N);
+    case 5: return cluster_applies_g<5>(N);
+    case 6: return cluster_applies_g<6>(N);
+    case 7: return cluster_applies_g<7>(N);
+    case 8: return cluster_applies_g<8>(N);
+    }
+    return false;
+}
+
+hipError_t launch_score_mfma(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
+                             float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
     switch (c->G) {
-    case 1: return launch_mfma_g<1>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 2: return launch_mfma_g<2>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 3: return launch_mfma_g<3>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 4: return launch_mfma_g<4>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 5: return launch_mfma_g<5>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 6: return launch_mfma_g<6>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 7: return launch_mfma_g<7>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
-    case 8: return launch_mfma_g<8>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
+    case 1: return launch_mfma_g<1>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 2: return launch_mfma_g<2>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 3: return launch_mfma_g<3>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 4: return launch_mfma_g<4>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 5: return launch_mfma_g<5>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 6: return launch_mfma_g<6>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 7: return launch_mfma_g<7>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 8: return launch_mfma_g<8>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
     }
     return hipErrorInvalidValue;
 }

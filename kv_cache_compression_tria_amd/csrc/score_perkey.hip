@@ -206,6 +206,7 @@ hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k
                                float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
     const bool pre_rope = (flags & TRIA_KEYS_PRE_ROPE) != 0;
+    if (!lay.has_raw) return hipErrorInvalidValue;   // the layout did not plan this path
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
     double *part = (double *)(ws + lay.part_off);
     hipError_t e = hipSuccess;

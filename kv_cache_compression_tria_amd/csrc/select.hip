@@ -73,7 +73,8 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
 }
 
 __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const float *__restrict__ F, int N, int B,
-                                                                       int32_t *__restrict__ kept)
+                                                                       int32_t *__restrict__ kept,
+                                                                       const int *__restrict__ guard)
 {
     constexpr int NT = kSelectThreads;
     constexpr int NW = NT / 64;
@@ -87,6 +88,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform loop bounds
     const float *f = F + (size_t)sid * N;
     int32_t *out = kept + (size_t)sid * B;            // B < N on this path
+    if (guard && *guard != 0) {                       // the scores are not usable: keep every row in place
+        for (int i = threadIdx.x; i < B; i += NT) out[i] = i;
+        return;
+    }
     auto key_at = [&](int j) -> uint32_t { return order_key(f[j]); };
     // wave w owns the contiguous key range [lo, hi); it walks it 256 keys per step, lane l taking
     // keys b + 64e + l (e < 4): four independent reads per step, visited in index order
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
 // slot #(key > T before j) + min(#(key == T before j), k).
 template <int NT>
 __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
-                                                        int32_t *__restrict__ kept)
+                                                        int32_t *__restrict__ kept, const int *__restrict__ guard)
 {
     constexpr int NW = NT / 64;
     extern __shared__ uint32_t keys[];                // [N]
@@ -282,6 +287,10 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float *f = F + (size_t)sid * N;
     int32_t *out = kept + (size_t)sid * B;            // B < N on this path
+    if (guard && *guard != 0) {                       // the scores are not usable: keep every row in place
+        for (int i = threadIdx.x; i < B; i += NT) out[i] = i;
+        return;
+    }
     const int nwords = (N + 31) >> 5;
     uint32_t *gtb = bm, *eqb = bm + nwords;
 
@@ -612,7 +621,7 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 //      kept index at #(key > T before j) + min(#(key == T before j), k).
 template <int NT>
 __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
-                                                           int32_t *__restrict__ kept)
+                                                           int32_t *__restrict__ kept, const int *__restrict__ guard)
 {
     constexpr int NW = NT / 64;
     constexpr int SMAX = kSelectSamples;
@@ -630,6 +639,10 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float *f = F + (size_t)sid * N;
     int32_t *out = kept + (size_t)sid * B;            // B < N on this path
+    if (guard && *guard != 0) {                       // the scores are not usable: keep every row in place
+        for (int i = threadIdx.x; i < B; i += NT) out[i] = i;
+        return;
+    }
     const int nwords = (N + 31) >> 5;
     uint32_t *gtb = bm, *eqb = bm + nwords;
 
@@ -898,7 +911,7 @@ __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N
     if (i < (size_t)n_streams * N) kept[i] = (int32_t)(i % N);
 }
 
-hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st)
+hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard, hipStream_t st)
 {
     KernelTimer timer(TRIA_TIMER_SELECT, st);
     if (B >= N) {
@@ -907,11 +920,11 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
         return hipGetLastError();
     }
     if (N <= kSelectShortKeys) {
-        select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept);
+        select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept, guard);
     } else if (N <= kSelectStreamKeys) {
-        select_stream_kernel<512><<<n_streams, 512, 0, st>>>(F, N, B, kept);
+        select_stream_kernel<512><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard);
     } else {
-        select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept);
+        select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept, guard);
     }
     return hipGetLastError();
 }

@@ -5,8 +5,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "../../include/tria.h"
 
 #define TRIA_D 128      // head_dim
@@ -36,6 +34,8 @@ struct tria_score_ws {
     size_t qrot_off, raw_off, part_off, zst_off, err_off, ops_off, pivot_off, xpart_off, arrive_off, total;
     int tiled;       // 1: the stream does not fit one block's LDS
     int tiles;       // key tiles (blocks) per stream on the tiled path
+    int cluster;     // 1: long bf16 streams are scored by stream clusters (xpart, arrive reserved)
+    int has_raw;     // 1: raw scores, tile partials and per-head mean / 1/std are reserved
 };
 
 namespace tria {
@@ -53,8 +53,6 @@ constexpr int kCompactRows = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-extern std::atomic<int> g_score_path;   // tria_score_path chosen by tria_set_score_path
-inline bool cluster_enabled() { return g_score_path.load() == TRIA_PATH_AUTO; }
 
 // Brackets the kernel launches of its scope with a HIP event pair on `st` when timing is enabled
 // (tria_timing_enable); does nothing otherwise.
@@ -71,7 +69,12 @@ class KernelTimer {
     hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 
-tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys);
+// Workspace layout of tria_score for these shapes and flags on the current device (the path choice
+// included); tria_score and the workspace sizers use the same function.
+tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys, unsigned flags);
+// True when bf16 streams of n_keys keys at group size G can be scored by stream clusters on the
+// current device (cooperative launch, clusters of at most 32 blocks).
+bool cluster_path_applies(int G, int n_keys);
 
 // Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once per (kernel, device);
 // thread-safe.
@@ -84,17 +87,18 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st);
 int mfma_ops_per_stream(int G);   // 16-byte operand words per lane and stream (prologue output)
-hipError_t launch_score_mfma(const tria_calib *c, const void *k, int n_seq, int N, const float *qrot, float *F,
-                             float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+// bf16 keys on the matrix cores: a prologue kernel rotates the queries (t, R-weighted with weight_r),
+// builds the operands and pivots and clears the error word, then the scoring kernels run
+hipError_t launch_score_mfma(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
+                             float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
 // per-head statistics and z-max of the tiled paths over raw [streams][G][N] and the tile partials
 // part [streams][tiles][G][4] (sums around pivot[stream][h], or around 0 when pivot is null)
 hipError_t launch_tile_finish(int G, int streams, int N, int tiles, const float *raw, const double *part,
                               const float *pivot, float *F, float *stats, const tria_score_ws &lay, char *ws,
                               hipStream_t st);
 // TRIA_OFFSET_MAX scoring (matrix cores, bf16 keys): the largest per-offset trigonometric series
-hipError_t launch_score_maxd(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, const float *qrot,
-                             bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws,
-                             hipStream_t st);
+hipError_t launch_score_maxd(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
+                             float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
 constexpr int kMaxdOffsetsLimit = 32;   // TRIA_OFFSET_MAX: most future offsets supported
 // TRIA_PER_KEY_PHASE / TRIA_KEYS_PRE_ROPE scoring (vector ALU, any dtype)
 hipError_t launch_score_perkey(const tria_calib *c, tria_dtype dt, const void *k, const int32_t *pos,
@@ -106,7 +110,9 @@ hipError_t launch_append(tria_dtype dt, void *k, void *v, int32_t *pos, int n_st
                          const void *kn, const void *vn, const int32_t *pn, int n_new, hipStream_t st);
 hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
                        float *stats, hipStream_t st);
-hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, hipStream_t st);
+// guard (device, may be null): when *guard != 0 at run time the kernels write kept = 0..B-1 (rows stay in
+// place) instead of selecting
+hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
 
