@@ -175,6 +175,28 @@ tria_status tria_prune(const tria_calib *calib, tria_dtype dtype, void *k, void 
 const char *tria_status_string(tria_status status);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): tria_prune with its workspace in a static device array
+ * of TRIA_STATIC_WORKSPACE_BYTES that the library holds on every device it runs on until the
+ * process ends; no call to hipMalloc or any other allocating routine is made (keep kernel timing
+ * off: its events are runtime allocations).  Same arguments and results as tria_prune, without ws.
+ * The caller still owns K, V, pos, t, F and kept.  When the workspace of all n_seq sequences does
+ * not fit the array, the step runs in chunks of whole sequences, one after the other on `stream`
+ * (same results).  Every call on a device shares that device's array: calls that overlap on one
+ * device (other streams or threads) race; calls ordered on one stream do not.
+ *   ws_used  (may be NULL) receives the array's device address: pass it to tria_score_check(ws_used,
+ *            256, stream) to confirm the step (as after tria_prune; on a failed score every row of
+ *            the affected sequences stays in place).  Valid until the next call on this device.
+ * Errors: those of tria_prune; TRIA_E_WORKSPACE when one sequence's workspace exceeds the array
+ * (e.g. the paths that stage raw scores in HBM at large N); TRIA_E_DEVICE when the array's address
+ * cannot be obtained.
+ */
+#define TRIA_STATIC_WORKSPACE_BYTES (64u << 20)
+tria_status tria_prune_static(const tria_calib *calib, tria_dtype dtype, void *k, void *v, int32_t *pos,
+                              const int32_t *t, int n_seq, int n_keys, int budget, float *F, int32_t *kept,
+                              unsigned flags, void **ws_used, void *stream);
+
+/*
  * Decode loop (the cadence of the 10100.com article, section "TriAttention方法", and of
  * watermelonwater.tech "TriAttention 方案设计" item 4: prune once every 128 generated tokens; the
  * attention layer of chenxutan.com/d/2624 section 4 appends each token's K/V and prunes back to

@@ -30,7 +30,7 @@ EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
-    "tria_calib_stats", "tria_append", "tria_decode_step",
+    "tria_calib_stats", "tria_append", "tria_decode_step", "tria_prune_static",
 )
 TIMERS = ("score_keys", "normalise", "select", "compact", "calib")
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.tria_decode_step.argtypes = [P, I, P, P, P, P, I, I, I, I, P, P, P, I, P, P, U, P, S,
                                        ctypes.POINTER(I), P]
         L.tria_calib_stats.argtypes = [I, P, I, I, I, I, P, P, P, P]
+        L.tria_prune_static.restype = I
+        L.tria_prune_static.argtypes = [P, I, P, P, P, P, I, I, I, P, P, U, ctypes.POINTER(P), P]
         L.tria_timing_read.restype = I
         L.tria_timing_read.argtypes = [ctypes.POINTER(D), ctypes.POINTER(I)]
         _lib = L
@@ -287,6 +289,38 @@ def prune(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int
     if check:
         score_check(ws, stream)
     return F, kept
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def prune_static(calib: Calib, k, v, pos, t, budget: int, F=None, kept=None, flags: int = 0, stream=None,
+                 check: bool = True):
+    """The prune step without a caller workspace (``tria_prune_static``): the library's static
+    device array of STATIC_WORKSPACE_BYTES serves as scratch, so the call allocates nothing (F and
+    kept must then be passed in by a caller that cannot allocate).  Returns (F, kept, ws_addr);
+    ws_addr is the device address of that array, for ``score_check_addr``.  With ``check`` (the
+    default) the call waits for the step and raises if the scoring failed on the device."""
+    import torch
+    S, L, Hkv, N, d = k.shape
+    for name, x in (("k", k), ("v", v), ("pos", pos), ("t", t), ("F", F), ("kept", kept)):
+        _dev(x, name)
+    if F is None:
+        F = torch.empty((S, L, Hkv, N), dtype=torch.float32, device=k.device)
+    if kept is None:
+        kept = torch.empty((S * L * Hkv, min(int(budget), N)), dtype=torch.int32, device=k.device)
+    addr = ctypes.c_void_p()
+    st = lib().tria_prune_static(calib.handle, _dtype_code(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(t), S, N,
+                                 int(budget), _ptr(F), _ptr(kept), int(flags), ctypes.byref(addr), _stream(stream))
+    _check(st, "tria_prune_static")
+    if check:
+        score_check_addr(addr.value, stream)
+    return F, kept, addr.value
+
+
+def score_check_addr(ws_addr: int, stream=None):
+    """``tria_score_check`` on a workspace given by its device address (as ``prune_static`` returns)."""
+    _check(lib().tria_score_check(ctypes.c_void_p(ws_addr), 256, _stream(stream)), "tria_score")
 
 
 def calib_stats(q, q_centre=None, q_band_norm=None, r_band=None, stream=None):
