@@ -40,11 +40,12 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
-def measured_traffic() -> dict:
+def measured_traffic(workload: str) -> dict:
     """HBM bytes per launch of each kernel as measured with rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy of known size), from the table in profiles/hbm_traffic.md.
-    A row counts only while the source file it was measured on is unchanged (its SHA-256 is in
-    the row); otherwise the figure is stale and is reported as null."""
+    A row counts only for the workload it was measured on and while the source file it was
+    measured on is unchanged (its SHA-256 is in the row); otherwise the figure is stale and is
+    reported as null."""
     import hashlib
 
     out = {}
@@ -55,9 +56,9 @@ def measured_traffic() -> dict:
         return out
     for line in lines:
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) < 4 or cells[0] != "traffic":
+        if len(cells) < 6 or cells[0] != "traffic" or cells[1] != workload:
             continue
-        name, nbytes, src, sha = cells[1], cells[2], cells[3], cells[4] if len(cells) > 4 else ""
+        name, nbytes, src, sha = cells[2], cells[3], cells[4], cells[5]
         try:
             with open(os.path.join(ROOT, src), "rb") as fh:
                 cur = hashlib.sha256(fh.read()).hexdigest()
@@ -314,7 +315,7 @@ def main():
                       {name: kv["ms_per_step"] for name, kv in kernels.items()}),
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kernels[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic().get(dom)},
+                     "unit": "GB/s", "frac": round(kernels[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name).get(dom)},
         "copy_GB_s": round(copy_gbs, 1),
         "alg_frac_of_copy": round(alg / (ms * 1e-3) / 1e9 / copy_gbs, 4),
         "placement": {"timed_cache": "allocated after the generated pristine copy (K, V, positions)",
@@ -450,7 +451,7 @@ def bench_calib(args, T, torch):
         "roofline": {"bound": "hbm", "kernel": "calib", "achieved": round(nbytes / (kms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic().get("calib")},
+                     "traffic": measured_traffic("qwen3-32b-calibration-64layer-64qhead-10240q-bf16").get("calib")},
     }
     if not args.no_cpu_baseline:
         from oracle import oracle
