@@ -103,6 +103,21 @@ tria_status tria_load_calib(tria_calib **out, int n_layers, int n_q_heads, int n
                             int n_offsets, void *stream);
 void tria_free_calib(tria_calib *calib);
 
+/*
+ * The per-band constants tria_load_calib builds its table from, computed on the host alone (no
+ * device work), f < head_dim/2:
+ *   w[f]  = fl32(rope_theta^(-2f/head_dim)) (the fp64 power rounded once to fp32);
+ *   C[f], S[f] = the mean over the offsets D of cos(w_f d) and sin(w_f d) (fp64; w_f d is exact in
+ *         fp64), the offset average of the trigonometric series (chenxutan.com/d/2624 section 3.3;
+ *         zhichai.net section "TriAttention：把理论变成算法" item 1);
+ *   nu[f] = w_f / 2pi as an unsigned 64-bit fraction of a turn, round(w_f / 2pi * 2^64): the phase
+ *         of an integer position n is then n * nu mod 2^64, exact in integer arithmetic.
+ * offsets / n_offsets as in tria_load_calib.  Outputs are host arrays of head_dim/2 elements.
+ * Errors: INVALID (null output, bad theta or offsets), UNSUPPORTED (head_dim != 128).
+ */
+tria_status tria_band_tables(double rope_theta, int head_dim, const int32_t *offsets, int n_offsets, double *w,
+                             double *C, double *S, uint64_t *nu);
+
 /* Shape queries of a loaded table (return -1 for a NULL handle). */
 int tria_calib_dim(const tria_calib *calib, int which /* 0 L, 1 Hq, 2 Hkv, 3 d, 4 G */);
 

@@ -30,7 +30,7 @@ EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
-    "tria_calib_stats", "tria_append", "tria_decode_step", "tria_prune_static",
+    "tria_calib_stats", "tria_append", "tria_decode_step", "tria_prune_static", "tria_band_tables",
 )
 TIMERS = ("score_keys", "normalise", "select", "compact", "calib")
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.tria_decode_step.argtypes = [P, I, P, P, P, P, I, I, I, I, P, P, P, I, P, P, U, P, S,
                                        ctypes.POINTER(I), P]
         L.tria_calib_stats.argtypes = [I, P, I, I, I, I, P, P, P, P]
+        L.tria_band_tables.restype = I
+        L.tria_band_tables.argtypes = [D, I, P, I, P, P, P, P]
         L.tria_prune_static.restype = I
         L.tria_prune_static.argtypes = [P, I, P, P, P, P, I, I, I, P, P, U, ctypes.POINTER(P), P]
         L.tria_timing_read.restype = I
@@ -161,6 +163,19 @@ class Calib:
             self.free()
         except Exception:
             pass
+
+
+def band_tables(rope_theta: float = 1e6, head_dim: int = 128, offsets=None):
+    """Host-only per-band constants (``tria_band_tables``): (w, C, S, nu) as numpy arrays of
+    head_dim/2 elements (float64, float64, float64, uint64)."""
+    h = head_dim // 2
+    w, C, S = (np.zeros(h, dtype=np.float64) for _ in range(3))
+    nu = np.zeros(h, dtype=np.uint64)
+    off = None if offsets is None else np.ascontiguousarray(offsets, dtype=np.int32)
+    _check(lib().tria_band_tables(float(rope_theta), int(head_dim), None if off is None else off.ctypes.data,
+                                  0 if off is None else len(off), w.ctypes.data, C.ctypes.data, S.ctypes.data,
+                                  nu.ctypes.data), "tria_band_tables")
+    return w, C, S, nu
 
 
 def load_calib(q_centre, q_band_norm, r_band, n_kv_heads: int, rope_theta: float = 1e6,

@@ -66,6 +66,35 @@ const char *tria_status_string(tria_status s)
     return "unknown status";
 }
 
+tria_status tria_band_tables(double theta, int d, const int32_t *offsets, int n_off, double *w, double *C, double *S,
+                             uint64_t *nu)
+{
+    if (!w || !C || !S || !nu || !(theta > 1.0) || !isfinite(theta)) return TRIA_E_INVALID;
+    if (n_off < 0 || (n_off > 0 && !offsets) || (n_off == 0 && offsets)) return TRIA_E_INVALID;
+    if (d != TRIA_D) return TRIA_E_UNSUPPORTED;
+    std::vector<int64_t> off;
+    if (n_off == 0) {
+        for (int i = 0; i <= 16; ++i) off.push_back(int64_t(1) << i);
+    } else {
+        for (int i = 0; i < n_off; ++i) {
+            if (offsets[i] < 0 || offsets[i] >= (1 << 24)) return TRIA_E_INVALID;
+            off.push_back(offsets[i]);
+        }
+    }
+    for (int f = 0; f < TRIA_HALF; ++f) {
+        w[f] = (double)(float)pow(theta, -2.0 * (double)f / (double)TRIA_D);
+        double c = 0.0, s = 0.0;
+        for (int64_t dd : off) {            // w_f * dd is exact in fp64 (24 + 24 bits)
+            c += cos(w[f] * (double)dd);
+            s += sin(w[f] * (double)dd);
+        }
+        C[f] = c / (double)off.size();
+        S[f] = s / (double)off.size();
+        nu[f] = turn_fraction(w[f]);
+    }
+    return TRIA_OK;
+}
+
 tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, const float *qc,
                             const float *qn, const float *rb, double theta, const int32_t *offsets,
                             int n_off, void *stream)
@@ -89,6 +118,13 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
             off.push_back(offsets[i]);
         }
     }
+    // Per-band constants in fp64: w_f, the offset mean of exp(i w_f d), the turn fraction.
+    double w[TRIA_HALF], C[TRIA_HALF], S[TRIA_HALF];
+    std::vector<uint64_t> nu(TRIA_HALF);
+    {
+        const tria_status st = tria_band_tables(theta, d, offsets, n_off, w, C, S, nu.data());
+        if (st != TRIA_OK) return st;
+    }
     const size_t nh = (size_t)L * Hq;
     for (size_t i = 0; i < nh * TRIA_D; ++i)
         if (!isfinite(qc[i])) return TRIA_E_INVALID;
@@ -97,20 +133,6 @@ tria_status tria_load_calib(tria_calib **out, int L, int Hq, int Hkv, int d, con
         if (!(rb[i] >= 0.f && rb[i] <= 1.f)) return TRIA_E_INVALID;
     }
 
-    // Per-band constants in fp64: w_f, the offset mean of exp(i w_f d), the turn fraction.
-    double w[TRIA_HALF], C[TRIA_HALF], S[TRIA_HALF];
-    std::vector<uint64_t> nu(TRIA_HALF);
-    for (int f = 0; f < TRIA_HALF; ++f) {
-        w[f] = (double)(float)pow(theta, -2.0 * (double)f / (double)TRIA_D);
-        double c = 0.0, s = 0.0;
-        for (int64_t dd : off) {            // w_f * dd is exact in fp64 (24 + 24 bits)
-            c += cos(w[f] * (double)dd);
-            s += sin(w[f] * (double)dd);
-        }
-        C[f] = c / (double)off.size();
-        S[f] = s / (double)off.size();
-        nu[f] = turn_fraction(w[f]);
-    }
     std::vector<double2> P(nh * TRIA_HALF);
     std::vector<float2> P32(nh * TRIA_HALF);
     std::vector<float> W(nh * TRIA_HALF);

@@ -21,6 +21,8 @@
 
 namespace tria {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint32_t order_key(float x)
 {
     uint32_t u = __float_as_uint(x);
@@ -51,7 +53,7 @@ constexpr int kCand = 4096;       // candidate list in LDS
 constexpr int kSelectDigitBins = 256;    // the sample's histogram and the bracketed keys' 8-bit digits
 constexpr int kSelectBitmapWords = 2 * ((kSelectStreamKeys + 31) / 32);
 constexpr int kSelectShortKeys = 8192;   // streams up to this many keys: LDS copy, 256-thread blocks
-constexpr int kSelectSamples = 1024;     // sampled scores behind the bracket
+constexpr int kSelectSamples = 2048;     // sampled scores behind the bracket (streamed selection)
 static_assert(kCand >= kBins0, "the fallback's histogram lives in the candidate keys");
 static_assert(kSelectBitmapWords >= kBins0, "the LDS selection's fallback histogram lives in the bitmap words");
 static_assert(kSelectShortKeys * 4 + (kSelectBitmapWords + kCand + kSelectDigitBins) * 4 + 1024 <= 64 * 1024,
@@ -473,10 +475,16 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
     }
 
     if (ok) {
-        // ---- the threshold among the candidates: four 8-bit digits
+        // ---- the threshold among the candidates: 8-bit digits.  Every candidate lies in [lo, hi),
+        // so the bits above the highest one in which lo and hi - 1 differ are common to all of them:
+        // the digits inside that prefix are skipped.
         const int nc = (int)s_ncand;
         k = (uint32_t)B - s_nabove;
-        for (int dgt = 0; dgt < 4; ++dgt) {
+        const uint32_t span_bits = s_lo ^ (s_hi - 1u);
+        const int first = span_bits ? 3 - ((31 - __builtin_clz(span_bits)) >> 3) : 3;
+        mask = first > 0 ? ~((1u << (32 - 8 * first)) - 1u) : 0u;
+        prefix = s_lo & mask;
+        for (int dgt = first; dgt < 4; ++dgt) {
             const int shift = 24 - 8 * dgt;
             for (int i = threadIdx.x; i < kSelectDigitBins; i += NT) dh[i] = 0u;
             __syncthreads();
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 
 // Streams up to 32768 keys are selected straight from F (no LDS copy of the keys, 42 KB of LDS, so
 // several streams run per CU and hide each other's memory latency):
-//   1. a strided sample of 1024 scores brackets the threshold: a 256-bin histogram of the sample,
+//   1. a strided sample of 2048 scores brackets the threshold: a 256-bin histogram of the sample,
 //      linear in the score between its extremes, gives the bins of the sample ranks e -/+ (4.5
 //      sigma + 2) from the top, where e = S B / N is the expected rank of the B-th largest key and
 //      sigma the spread of that binomial count; their edges are the bounds lo <= hi;
@@ -619,12 +627,12 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 //      re-reading F, and a bitmap pass follows;
 //   4. thread w takes bitmap word w: a block-wide prefix of the words' bit counts places every
 //      kept index at #(key > T before j) + min(#(key == T before j), k).
-template <int NT>
+// SMAX: sampled scores behind the bracket; DEPTH: 16-byte loads of F in flight per lane in the pass
+template <int NT, int SMAX, int DEPTH>
 __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
                                                            int32_t *__restrict__ kept, const int *__restrict__ guard)
 {
     constexpr int NW = NT / 64;
-    constexpr int SMAX = kSelectSamples;
     constexpr int SPT = (SMAX + NT - 1) / NT;         // samples per thread
     __shared__ uint32_t bm[kSelectBitmapWords];       // the two bitmaps
     __shared__ uint32_t ckey[kCand];                  // candidates' keys; the fallback's histogram
@@ -759,20 +767,8 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     if (ok) {
         const uint32_t blo = s_lo, bhi = s_hi;
         uint32_t nabove = 0u;
-        // a wave step covers 256 keys: lane l holds keys 4l .. 4l + 3 of the step
-        for (int c0 = wid * 256; c0 < N; c0 += NT * 4) {
-            uint32_t u[4];
-            if (vec) {
-                const int i4 = (c0 >> 2) + lane;
-                const float4 v = 4 * i4 < N ? ((const float4 *)f)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
-                u[0] = order_key(v.x); u[1] = order_key(v.y); u[2] = order_key(v.z); u[3] = order_key(v.w);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = c0 + 4 * lane + e;
-                    u[e] = j < N ? order_key(f[j]) : 0u;
-                }
-            }
+        // one wave step of 256 keys (lane l holds keys c0 + 4l .. c0 + 4l + 3)
+        auto step = [&](int c0, const uint32_t (&u)[4]) {
             uint32_t nib = 0u;
             uint64_t bc[4];
             uint32_t tot = 0u;
@@ -812,6 +808,37 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
                     base += (uint32_t)__builtin_popcountll(bc[e]);
                 }
             }
+        };
+        if (vec) {
+            // DEPTH steps' loads are issued before the first of them is used; buffer loads over the
+            // stream's N scores (the whole offset in the range-checked vector offset) return zero
+            // past the end, so the loads need no branches
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)f, 0, N * 4, 0x00020000);
+            for (int c0 = wid * 256; c0 < N; c0 += DEPTH * NT * 4) {
+                u32x4 x[DEPTH];
+#pragma unroll
+                for (int q = 0; q < DEPTH; ++q)
+                    x[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (c0 + q * NT * 4 + 4 * lane), 0, 0);
+#pragma unroll
+                for (int q = 0; q < DEPTH; ++q) {
+                    const int c = c0 + q * NT * 4;
+                    if (c < N) {                              // uniform
+                        const uint32_t u[4] = {order_key(__uint_as_float(x[q][0])), order_key(__uint_as_float(x[q][1])),
+                                               order_key(__uint_as_float(x[q][2])), order_key(__uint_as_float(x[q][3]))};
+                        step(c, u);
+                    }
+                }
+            }
+        } else {
+            for (int c0 = wid * 256; c0 < N; c0 += NT * 4) {
+                uint32_t u[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = c0 + 4 * lane + e;
+                    u[e] = j < N ? order_key(f[j]) : 0u;
+                }
+                step(c0, u);
+            }
         }
         if (lane == 0 && nabove) atomicAdd(&s_nabove, nabove);
         __syncthreads();
@@ -820,10 +847,16 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     }
 
     if (ok) {
-        // ---- the threshold among the candidates: four 8-bit digits
+        // ---- the threshold among the candidates: 8-bit digits.  Every candidate lies in [lo, hi),
+        // so the bits above the highest one in which lo and hi - 1 differ are common to all of them:
+        // the digits inside that prefix are skipped.
         const int nc = (int)s_ncand;
         k = (uint32_t)B - s_nabove;
-        for (int dgt = 0; dgt < 4; ++dgt) {
+        const uint32_t span_bits = s_lo ^ (s_hi - 1u);
+        const int first = span_bits ? 3 - ((31 - __builtin_clz(span_bits)) >> 3) : 3;
+        mask = first > 0 ? ~((1u << (32 - 8 * first)) - 1u) : 0u;
+        prefix = s_lo & mask;
+        for (int dgt = first; dgt < 4; ++dgt) {
             const int shift = 24 - 8 * dgt;
             for (int i = threadIdx.x; i < kSelectDigitBins; i += NT) dh[i] = 0u;
             __syncthreads();
@@ -922,7 +955,7 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
     if (N <= kSelectShortKeys) {
         select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept, guard);
     } else if (N <= kSelectStreamKeys) {
-        select_stream_kernel<512><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard);
+        select_stream_kernel<512, kSelectSamples, 4><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard);
     } else {
         select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept, guard);
     }
