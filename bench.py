@@ -275,6 +275,7 @@ def main():
         "normalise": n_streams * N * 4,         # F written once
         "select": n_streams * N * 4,            # F read once
         "compact": moved * (4 * r + 8),         # moved K, V rows and positions, read + written
+        "select_compact": n_streams * N * 4 + moved * (4 * r + 8),   # both, in one kernel (tria_prune)
     }
     kernels = {}
     for name, kv in kern.items():

@@ -32,7 +32,7 @@ EXPORTED = (
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
     "tria_calib_stats", "tria_append", "tria_decode_step", "tria_prune_static", "tria_band_tables",
 )
-TIMERS = ("score_keys", "normalise", "select", "compact", "calib")
+TIMERS = ("score_keys", "normalise", "select", "compact", "calib", "select_compact")
 
 
 class TriaError(RuntimeError):

@@ -331,13 +331,22 @@ tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int
                        const int32_t *t, int n_seq, int N, int B, float *F, int32_t *kept,
                        unsigned flags, void *ws, size_t ws_bytes, void *stream)
 {
-    if (!c || !kept || B <= 0) return TRIA_E_INVALID;
+    if (!c || !kept || !v || B <= 0) return TRIA_E_INVALID;
+    // the compaction's checks, before anything is launched
+    if (!aligned(v, 16) || (pos && !aligned(pos, 4)) || !aligned(kept, 4)) return TRIA_E_INVALID;
     tria_status s = tria_score(c, dt, k, pos, t, n_seq, N, F, nullptr, nullptr, flags, ws, ws_bytes, stream);
     if (s != TRIA_OK) return s;
     const int n_streams = n_seq * c->L * c->Hkv;
     // the selection reads the score's error word: after a failed score it keeps every row in place,
     // so that the compaction moves nothing
     const int *guard = (const int *)((const char *)ws + tria::score_ws_layout(c, dt, n_seq, N, flags).err_off);
+    if (tria::select_compact_fused(N, B)) {
+        // selection and compaction in one kernel (same results as the two calls)
+        if (tria::launch_select_compact(dt, F, n_streams, N, B, kept, guard, k, v, pos, (hipStream_t)stream) !=
+            hipSuccess)
+            return TRIA_E_DEVICE;
+        return TRIA_OK;
+    }
     if (tria::launch_select(F, n_streams, N, B, kept, guard, (hipStream_t)stream) != hipSuccess)
         return TRIA_E_DEVICE;
     return tria_compact(dt, k, v, pos, kept, n_streams, N, B, TRIA_D, stream);

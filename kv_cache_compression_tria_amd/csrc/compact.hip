@@ -1,99 +1,16 @@
-// compact.hip -- in-place, order-preserving compaction of K, V and positions (gfx950).
-//
-// After selection, row i of each kept tensor takes row kept[i] (i < B) (chenxutan.com/d/2624
-// section 4.2: the cache is indexed by the sorted kept indices).  kept is strictly ascending,
-// so kept[i] >= i: every source lies at or after its destination.  One workgroup per stream
-// walks destination tiles in order; within a tile every thread first loads all of its source
-// rows into registers, the workgroup synchronises, and only then are the rows written.  A
-// tile's destinations [i0, i0+T) lie below every later tile's sources (>= i0+T), and earlier
-// tiles are complete, so no row is overwritten before it has been read.  Rows already in place
-// (kept[i] == i) are not touched.
-#include "common.cuh"
+// compact.hip -- in-place, order-preserving compaction of K, V and positions (gfx950): one block
+// per stream (the method and its ordering argument are in compact_stream.cuh).
+#include "compact_stream.cuh"
 #include "tria_internal.h"
 
 namespace tria {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// RV: 16-byte words per row (16 for bf16, 32 for fp32; head_dim 128).  Thread x of the block handles
-// words x + m kCompactThreads (m < PER) of a tile of kCompactRows destination rows.  The kept
-// indices of the next tile are loaded while the current tile's rows are in flight (a load of an
-// index and then of the row it names would otherwise be two memory latencies per tile), and rows
-// move with non-temporal loads and stores: nothing here is read again soon.
 template <int RV>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(uint4 *__restrict__ k, uint4 *__restrict__ v,
                                                                   int32_t *__restrict__ pos,
                                                                   const int32_t *__restrict__ kept, int N, int nk)
 {
-    constexpr int T = kCompactRows;
-    constexpr int NT = kCompactThreads;
-    constexpr int PER = T * RV / NT;                  // 16-byte words per thread per tensor
-    const int sid = blockIdx.x;
-    uint4 *kb = k + (size_t)sid * N * RV;
-    uint4 *vb = v + (size_t)sid * N * RV;
-    int32_t *pb = pos ? pos + (size_t)sid * N : nullptr;
-    const int32_t *kp = kept + (size_t)sid * nk;
-    // source rows of the words this thread moves in the tile at i0 (a row past nk names itself)
-    int src[PER];
-    int psrc = 0;
-    auto fetch_sources = [&](int i0) {
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int r = i0 + (threadIdx.x + m * NT) / RV;
-            src[m] = r < nk ? kp[r] : r;
-        }
-        if (pb && threadIdx.x < T) {
-            const int r = i0 + threadIdx.x;
-            psrc = r < nk ? kp[r] : r;
-        }
-    };
-    fetch_sources(0);
-    for (int i0 = 0; i0 < nk; i0 += T) {
-        uint4 bk[PER], bv[PER];
-        bool mv[PER];
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int idx = threadIdx.x + m * NT;
-            const int r = i0 + idx / RV, c = idx % RV;
-            const int s = src[m];
-            mv[m] = r < nk && s > r && s < N;         // valid kept[] has r <= s < N; s == r stays
-            if (mv[m]) {
-                const u32x4 a = __builtin_nontemporal_load((const u32x4 *)&kb[(size_t)s * RV + c]);
-                const u32x4 b = __builtin_nontemporal_load((const u32x4 *)&vb[(size_t)s * RV + c]);
-                bk[m] = make_uint4(a[0], a[1], a[2], a[3]);
-                bv[m] = make_uint4(b[0], b[1], b[2], b[3]);
-            }
-        }
-        int32_t pv = 0;
-        bool pmv = false;
-        if (pb && threadIdx.x < T) {
-            const int r = i0 + threadIdx.x;
-            if (r < nk && psrc > r && psrc < N) {
-                pmv = true;
-                pv = pb[psrc];
-            }
-        }
-        if (i0 + T < nk) fetch_sources(i0 + T);
-        // every source value of this tile must be in registers before anyone writes
-#pragma unroll
-        for (int m = 0; m < PER; ++m)
-            if (mv[m]) {
-                hold(bk[m]);
-                hold(bv[m]);
-            }
-        if (pmv) hold((uint32_t)pv);
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            if (mv[m]) {
-                const int idx = threadIdx.x + m * NT;
-                const int r = i0 + idx / RV, c = idx % RV;
-                __builtin_nontemporal_store(u32x4{bk[m].x, bk[m].y, bk[m].z, bk[m].w}, (u32x4 *)&kb[(size_t)r * RV + c]);
-                __builtin_nontemporal_store(u32x4{bv[m].x, bv[m].y, bv[m].z, bv[m].w}, (u32x4 *)&vb[(size_t)r * RV + c]);
-            }
-        }
-        if (pmv) pb[i0 + threadIdx.x] = pv;
-    }
+    compact_stream<RV, kCompactThreads, kCompactRows>(blockIdx.x, k, v, pos, kept, N, nk);
 }
 
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept, int n_streams,

@@ -17,6 +17,7 @@
 //     candidate list and the output are written in index order from per-wave counts and a prefix
 //     over the 16 wave totals.
 #include "common.cuh"
+#include "compact_stream.cuh"
 #include "tria_internal.h"
 
 namespace tria {
@@ -627,10 +628,11 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 //      re-reading F, and a bitmap pass follows;
 //   4. thread w takes bitmap word w: a block-wide prefix of the words' bit counts places every
 //      kept index at #(key > T before j) + min(#(key == T before j), k).
-// SMAX: sampled scores behind the bracket; DEPTH: 16-byte loads of F in flight per lane in the pass
+// The selection of stream sid by one block of NT threads (every thread must call it).  SMAX:
+// sampled scores behind the bracket; DEPTH: 16-byte loads of F in flight per lane in the pass.
 template <int NT, int SMAX, int DEPTH>
-__global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
-                                                           int32_t *__restrict__ kept, const int *__restrict__ guard)
+__device__ __forceinline__ void select_stream_block(int sid, const float *__restrict__ F, int N, int B,
+                                                    int32_t *__restrict__ kept, const int *__restrict__ guard)
 {
     constexpr int NW = NT / 64;
     constexpr int SPT = (SMAX + NT - 1) / NT;         // samples per thread
@@ -642,7 +644,6 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     __shared__ float s_min[NW], s_max[NW];
     __shared__ uint32_t s_prefix, s_k, s_ncand, s_nabove, s_lo, s_hi;
 
-    const int sid = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float *f = F + (size_t)sid * N;
@@ -938,10 +939,53 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     }
 }
 
+template <int NT, int SMAX, int DEPTH>
+__global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
+                                                           int32_t *__restrict__ kept, const int *__restrict__ guard)
+{
+    select_stream_block<NT, SMAX, DEPTH>(blockIdx.x, F, N, B, kept, guard);
+}
+
+// The prune step's selection and compaction in one kernel, one block per stream: the block
+// selects its stream's kept keys (written to kept), then compacts the stream's K, V and positions
+// by them.  While some blocks of a CU select (bound by instruction issue and memory latency)
+// others move rows (bound by HBM bandwidth), and the kept indices are read back while they are
+// still in the caches.
+constexpr int kSelectCompactThreads = 512;
+
+template <int RV>
+__global__ __launch_bounds__(kSelectCompactThreads) void select_compact_kernel(const float *__restrict__ F, int N, int B,
+                                                                            int32_t *__restrict__ kept,
+                                                                            const int *__restrict__ guard,
+                                                                            uint4 *__restrict__ k, uint4 *__restrict__ v,
+                                                                            int32_t *__restrict__ pos)
+{
+    constexpr int NT = kSelectCompactThreads;
+    select_stream_block<NT, kSelectSamples, 4>(blockIdx.x, F, N, B, kept, guard);
+    __syncthreads();   // the kept indices written by every thread are visible to the whole block
+    compact_stream<RV, NT, 2 * kCompactRows>(blockIdx.x, k, v, pos, kept, N, B);
+}
+
 __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < (size_t)n_streams * N) kept[i] = (int32_t)(i % N);
+}
+
+bool select_compact_fused(int N, int B) { return B < N && N > kSelectShortKeys && N <= kSelectStreamKeys; }
+
+hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, int N, int B, int32_t *kept,
+                                 const int *guard, void *k, void *v, int32_t *pos, hipStream_t st)
+{
+    if (!select_compact_fused(N, B)) return hipErrorInvalidValue;
+    KernelTimer timer(TRIA_TIMER_SELECT_COMPACT, st);
+    if (dt == TRIA_BF16)
+        select_compact_kernel<16><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, (uint4 *)k,
+                                                                             (uint4 *)v, pos);
+    else
+        select_compact_kernel<32><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, (uint4 *)k,
+                                                                             (uint4 *)v, pos);
+    return hipGetLastError();
 }
 
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard, hipStream_t st)

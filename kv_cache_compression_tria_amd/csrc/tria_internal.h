@@ -115,5 +115,9 @@ hipError_t launch_zmax(int G, const float *raw, const double *part, int streams,
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
+// selection and compaction in one kernel (tria_prune) for the shapes where select_compact_fused holds
+bool select_compact_fused(int N, int B);
+hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, int N, int B, int32_t *kept,
+                                 const int *guard, void *k, void *v, int32_t *pos, hipStream_t st);
 
 }  // namespace tria
