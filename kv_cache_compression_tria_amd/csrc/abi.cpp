@@ -301,7 +301,7 @@ tria_status tria_select_topB(const float *F, int n_streams, int N, int B, int32_
     if (!F || !kept || n_streams <= 0 || N <= 0 || B <= 0 || N > (1 << 24)) return TRIA_E_INVALID;
     if (!aligned(F, 4) || !aligned(kept, 4)) return TRIA_E_INVALID;
     if (ws_bytes < tria_select_workspace_bytes(n_streams, N, B) || !ws) return TRIA_E_WORKSPACE;
-    if (tria::launch_select(F, n_streams, N, B, kept, nullptr, (hipStream_t)stream) != hipSuccess)
+    if (tria::launch_select(F, n_streams, N, B, kept, nullptr, nullptr, (hipStream_t)stream) != hipSuccess)
         return TRIA_E_DEVICE;
     return TRIA_OK;
 }
@@ -339,15 +339,18 @@ tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int
     const int n_streams = n_seq * c->L * c->Hkv;
     // the selection reads the score's error word: after a failed score it keeps every row in place,
     // so that the compaction moves nothing
-    const int *guard = (const int *)((const char *)ws + tria::score_ws_layout(c, dt, n_seq, N, flags).err_off);
+    const tria_score_ws lay = tria::score_ws_layout(c, dt, n_seq, N, flags);
+    const int *guard = (const int *)((const char *)ws + lay.err_off);
+    // the stream-cluster scorers leave a side copy of every 16th score, which the selection samples
+    const float *samp = lay.cluster ? (const float *)((const char *)ws + lay.samp_off) : nullptr;
     if (tria::select_compact_fused(N, B)) {
         // selection and compaction in one kernel (same results as the two calls)
-        if (tria::launch_select_compact(dt, F, n_streams, N, B, kept, guard, k, v, pos, (hipStream_t)stream) !=
-            hipSuccess)
+        if (tria::launch_select_compact(dt, F, n_streams, N, B, kept, guard, samp, k, v, pos,
+                                        (hipStream_t)stream) != hipSuccess)
             return TRIA_E_DEVICE;
         return TRIA_OK;
     }
-    if (tria::launch_select(F, n_streams, N, B, kept, guard, (hipStream_t)stream) != hipSuccess)
+    if (tria::launch_select(F, n_streams, N, B, kept, guard, samp, (hipStream_t)stream) != hipSuccess)
         return TRIA_E_DEVICE;
     return tria_compact(dt, k, v, pos, kept, n_streams, N, B, TRIA_D, stream);
 }

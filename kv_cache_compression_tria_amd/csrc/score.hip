@@ -53,12 +53,15 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
         off += align256(heads * sizeof(float));
     }
     if (w.cluster) {
-        // partial sums exchanged inside stream clusters (two round slots per block) and the
-        // clusters' arrival counters (one per cluster) or flags (one per block)
+        // partial sums exchanged inside stream clusters (two round slots per block), the clusters'
+        // arrival counters (one per cluster) or flags (one per block)
         w.xpart_off = off;
         off += align256((size_t)kClusterMaxBlocks * 2 * TRIA_MAX_G * 4 * sizeof(double));
         w.arrive_off = off;
         off += align256((size_t)kClusterMaxBlocks * sizeof(uint32_t));
+        // the side copy of every kSampleStride-th F, which the selection samples
+        w.samp_off = off;
+        off += align256(streams * (size_t)((N + kSampleStride - 1) / kSampleStride) * sizeof(float));
     }
     if (w.has_raw) {
         // raw scores [streams][G][N], tile partials and per-head mean / 1/std

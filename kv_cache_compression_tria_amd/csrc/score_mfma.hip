@@ -652,7 +652,8 @@ template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
     int streams, int Ps, int Kb, int cpx, int C, double *__restrict__ xpart, uint32_t *__restrict__ arrive,
-    float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats, int *__restrict__ err)
+    float *__restrict__ F, float *__restrict__ samp, float *__restrict__ raw_out, float *__restrict__ stats,
+    int *__restrict__ err)
 {
     constexpr int GP = (G + 1) & ~1;
     extern __shared__ float lraw[];                // [Kb][GP]
@@ -775,11 +776,13 @@ __global__ __launch_bounds__(NW * 64) void score_mfma_cluster_kernel(
         }
         __syncthreads();
         float *fo = F + (size_t)sid * N + j0;
+        float *so = samp + (size_t)sid * ((N + kSampleStride - 1) / kSampleStride) + j0 / kSampleStride;
         for (int j = threadIdx.x; j < nkeys; j += NW * 64) {
             float z = -INFINITY;
 #pragma unroll
             for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[j * GP + h] - zmu[h]) * zinv[h]);
             fo[j] = z;
+            if (j % kSampleStride == 0) so[j / kSampleStride] = z;   // j0 is a multiple of the stride
         }
         if (raw_out)
             for (int q = threadIdx.x; q < G * nkeys; q += NW * 64) {
@@ -918,7 +921,8 @@ template <int G, int NTC>
 __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
     int streams, int Ps, int Kb, int cpx, int C, double *__restrict__ xpart, uint32_t *__restrict__ arrive,
-    float *__restrict__ F, float *__restrict__ raw_out, float *__restrict__ stats, int *__restrict__ err)
+    float *__restrict__ F, float *__restrict__ samp, float *__restrict__ raw_out, float *__restrict__ stats,
+    int *__restrict__ err)
 {
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
@@ -1206,6 +1210,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         asm volatile("" ::: "memory");   // zmu and zinv are read after the stamp
         const int jr = prt(r) * Kb, nkr = nk_of(r);
         float *fo = F + (size_t)sid * N + jr;
+        float *so = samp + (size_t)sid * ((N + kSampleStride - 1) / kSampleStride) + jr / kSampleStride;
         for (int idx = lane; idx < nt * 16; idx += 64) {
             const int key = tile_of(idx >> 4) * 16 + (idx & 15);
             if (key < nkr) {
@@ -1213,6 +1218,9 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 #pragma unroll
                 for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[key * GP + h] - zmu[h]) * zinv[h]);
                 __builtin_nontemporal_store(z, &fo[key]);   // read back by the selection, not now
+                // the first key of each 16-key tile (jr is a multiple of 16) to the side sample
+                static_assert(kSampleStride == 16, "one sampled key per 16-key tile");
+                if ((idx & 15) == 0) __builtin_nontemporal_store(z, &so[key >> 4]);
                 if (raw_out)
 #pragma unroll
                     for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + jr + key] = lraw[key * GP + h];
@@ -1342,9 +1350,12 @@ static hipError_t launch_cluster_g(const ClusterPlan &pl, const u32x4 *kp, const
     uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);   // one counter per cluster, cleared by the prologue
     double *xpart = (double *)(ws + lay.xpart_off);
     int *err = (int *)(ws + lay.err_off);
+    float *samp = (float *)(ws + lay.samp_off);
     int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
-    void *args[] = {(void *)&kp, (void *)&ops, (void *)&pivot, &n, &S, &Ps, &Kb, &cpx, &C,
-                    (void *)&xpart, (void *)&arrive, (void *)&F, (void *)&raw_out, (void *)&stats, (void *)&err};
+    void *args[] = {(void *)&kp,    (void *)&ops,   (void *)&pivot, &n,
+                    &S,             &Ps,            &Kb,            &cpx,
+                    &C,             (void *)&xpart, (void *)&arrive, (void *)&F,
+                    (void *)&samp,  (void *)&raw_out, (void *)&stats, (void *)&err};
     KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
     return hipLaunchCooperativeKernel((const void *)score_mfma_cluster_kernel<G, NW>, dim3(pl.nb), dim3(NW * 64),
                                       args, (unsigned)lds, st);
@@ -1421,9 +1432,12 @@ static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u
     uint32_t *arrive = (uint32_t *)(ws + lay.arrive_off);   // one flag per block, cleared by the prologue
     double *xpart = (double *)(ws + lay.xpart_off);
     int *err = (int *)(ws + lay.err_off);
+    float *samp = (float *)(ws + lay.samp_off);
     int n = N, S = streams, Ps = pl.Ps, Kb = pl.Kb, cpx = pl.cpx, C = pl.C;
-    void *args[] = {(void *)&kp, (void *)&ops, (void *)&pivot, &n, &S, &Ps, &Kb, &cpx, &C,
-                    (void *)&xpart, (void *)&arrive, (void *)&F, (void *)&raw_out, (void *)&stats, (void *)&err};
+    void *args[] = {(void *)&kp,    (void *)&ops,   (void *)&pivot, &n,
+                    &S,             &Ps,            &Kb,            &cpx,
+                    &C,             (void *)&xpart, (void *)&arrive, (void *)&F,
+                    (void *)&samp,  (void *)&raw_out, (void *)&stats, (void *)&err};
     // every block full (the first and the last part of a stream run the same item count): the
     // variant with that count built in
     auto items = [](int nkeys) { return std::max(1, ((nkeys + 15) / 16 + NW - 1) / NW); };

@@ -614,7 +614,9 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 
 // Streams up to 32768 keys are selected straight from F (no LDS copy of the keys, 42 KB of LDS, so
 // several streams run per CU and hide each other's memory latency):
-//   1. a strided sample of 2048 scores brackets the threshold: a 256-bin histogram of the sample,
+//   1. a sample of up to 2048 scores brackets the threshold (the scorer's side copy of every 16th
+//      score when the caller passes one, read contiguously; else every (N / 2048)-th score of F,
+//      which touches every line of F once more): a 256-bin histogram of the sample,
 //      linear in the score between its extremes, gives the bins of the sample ranks e -/+ (4.5
 //      sigma + 2) from the top, where e = S B / N is the expected rank of the B-th largest key and
 //      sigma the spread of that binomial count; their edges are the bounds lo <= hi;
@@ -630,9 +632,12 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
 //      kept index at #(key > T before j) + min(#(key == T before j), k).
 // The selection of stream sid by one block of NT threads (every thread must call it).  SMAX:
 // sampled scores behind the bracket; DEPTH: 16-byte loads of F in flight per lane in the pass.
+// samp (may be null): per stream, ceil(N / kSampleStride) scores, samp[s][i] = F[s][kSampleStride i].
+// The sample only places the bracket: the selection is exact whatever it holds.
 template <int NT, int SMAX, int DEPTH>
 __device__ __forceinline__ void select_stream_block(int sid, const float *__restrict__ F, int N, int B,
-                                                    int32_t *__restrict__ kept, const int *__restrict__ guard)
+                                                    int32_t *__restrict__ kept, const int *__restrict__ guard,
+                                                    const float *__restrict__ samp)
 {
     constexpr int NW = NT / 64;
     constexpr int SPT = (SMAX + NT - 1) / NT;         // samples per thread
@@ -688,9 +693,11 @@ __device__ __forceinline__ void select_stream_block(int sid, const float *__rest
         k = s_k;
     };
 
-    // ---- the bracket from a strided sample of the scores
-    const int S = min(N, SMAX);
-    const int stride = N / S;
+    // ---- the bracket from a sample of the scores: the side copy, else a strided read of F
+    const int ns = (N + kSampleStride - 1) / kSampleStride;
+    const float *sp = samp ? samp + (size_t)sid * ns : f;
+    const int S = min(samp ? ns : N, SMAX);
+    const int stride = samp ? 1 : N / S;
     float sv[SPT];
     bool smp[SPT];
     float lo = INFINITY, hi = -INFINITY;
@@ -698,7 +705,7 @@ __device__ __forceinline__ void select_stream_block(int sid, const float *__rest
     for (int q = 0; q < SPT; ++q) {
         const int t = q * NT + threadIdx.x;
         smp[q] = t < S;
-        sv[q] = smp[q] ? f[(size_t)t * stride] : 0.f;
+        sv[q] = smp[q] ? sp[(size_t)t * stride] : 0.f;
         if (smp[q]) {
             if (isfinite(sv[q])) {
                 lo = fminf(lo, sv[q]);
@@ -941,9 +948,10 @@ __device__ __forceinline__ void select_stream_block(int sid, const float *__rest
 
 template <int NT, int SMAX, int DEPTH>
 __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
-                                                           int32_t *__restrict__ kept, const int *__restrict__ guard)
+                                                           int32_t *__restrict__ kept, const int *__restrict__ guard,
+                                                           const float *__restrict__ samp)
 {
-    select_stream_block<NT, SMAX, DEPTH>(blockIdx.x, F, N, B, kept, guard);
+    select_stream_block<NT, SMAX, DEPTH>(blockIdx.x, F, N, B, kept, guard, samp);
 }
 
 // The prune step's selection and compaction in one kernel, one block per stream: the block
@@ -957,11 +965,12 @@ template <int RV>
 __global__ __launch_bounds__(kSelectCompactThreads) void select_compact_kernel(const float *__restrict__ F, int N, int B,
                                                                             int32_t *__restrict__ kept,
                                                                             const int *__restrict__ guard,
+                                                                            const float *__restrict__ samp,
                                                                             uint4 *__restrict__ k, uint4 *__restrict__ v,
                                                                             int32_t *__restrict__ pos)
 {
     constexpr int NT = kSelectCompactThreads;
-    select_stream_block<NT, kSelectSamples, 4>(blockIdx.x, F, N, B, kept, guard);
+    select_stream_block<NT, kSelectSamples, 4>(blockIdx.x, F, N, B, kept, guard, samp);
     __syncthreads();   // the kept indices written by every thread are visible to the whole block
     compact_stream<RV, NT, 2 * kCompactRows>(blockIdx.x, k, v, pos, kept, N, B);
 }
@@ -975,20 +984,21 @@ __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N
 bool select_compact_fused(int N, int B) { return B < N && N > kSelectShortKeys && N <= kSelectStreamKeys; }
 
 hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, int N, int B, int32_t *kept,
-                                 const int *guard, void *k, void *v, int32_t *pos, hipStream_t st)
+                                 const int *guard, const float *samp, void *k, void *v, int32_t *pos, hipStream_t st)
 {
     if (!select_compact_fused(N, B)) return hipErrorInvalidValue;
     KernelTimer timer(TRIA_TIMER_SELECT_COMPACT, st);
     if (dt == TRIA_BF16)
-        select_compact_kernel<16><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, (uint4 *)k,
-                                                                             (uint4 *)v, pos);
+        select_compact_kernel<16><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, samp,
+                                                                             (uint4 *)k, (uint4 *)v, pos);
     else
-        select_compact_kernel<32><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, (uint4 *)k,
-                                                                             (uint4 *)v, pos);
+        select_compact_kernel<32><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, samp,
+                                                                             (uint4 *)k, (uint4 *)v, pos);
     return hipGetLastError();
 }
 
-hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard, hipStream_t st)
+hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard,
+                         const float *samp, hipStream_t st)
 {
     KernelTimer timer(TRIA_TIMER_SELECT, st);
     if (B >= N) {
@@ -999,7 +1009,7 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
     if (N <= kSelectShortKeys) {
         select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept, guard);
     } else if (N <= kSelectStreamKeys) {
-        select_stream_kernel<512, kSelectSamples, 4><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard);
+        select_stream_kernel<512, kSelectSamples, 4><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard, samp);
     } else {
         select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept, guard);
     }

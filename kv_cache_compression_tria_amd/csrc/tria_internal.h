@@ -31,10 +31,10 @@ struct tria_calib {
 
 // Workspace layout of tria_score (every region 256-byte aligned).
 struct tria_score_ws {
-    size_t qrot_off, raw_off, part_off, zst_off, err_off, ops_off, pivot_off, xpart_off, arrive_off, total;
+    size_t qrot_off, raw_off, part_off, zst_off, err_off, ops_off, pivot_off, xpart_off, arrive_off, samp_off, total;
     int tiled;       // 1: the stream does not fit one block's LDS
     int tiles;       // key tiles (blocks) per stream on the tiled path
-    int cluster;     // 1: long bf16 streams are scored by stream clusters (xpart, arrive reserved)
+    int cluster;     // 1: long bf16 streams are scored by stream clusters (xpart, arrive, samp reserved)
     int has_raw;     // 1: raw scores, tile partials and per-head mean / 1/std are reserved
 };
 
@@ -48,6 +48,7 @@ constexpr int kClusterMaxBlocks = 1024;   // largest cluster grid the workspace 
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectStreamKeys = 32768;  // streams up to this many keys: the streamed selection (bitmaps of
                                           // 2 x N/32 words in LDS)
+constexpr int kSampleStride = 16;     // the cluster scorers copy every 16th key's F to a side sample
 constexpr int kCompactThreads = 256;
 constexpr int kCompactRows = 64;
 
@@ -111,13 +112,17 @@ hipError_t launch_append(tria_dtype dt, void *k, void *v, int32_t *pos, int n_st
 hipError_t launch_zmax(int G, const float *raw, const double *part, int streams, int N, int tiles, float *F,
                        float *stats, hipStream_t st);
 // guard (device, may be null): when *guard != 0 at run time the kernels write kept = 0..B-1 (rows stay in
-// place) instead of selecting
-hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard, hipStream_t st);
+// place) instead of selecting.  samp (device, may be null): the cluster scorers' side copy of every
+// kSampleStride-th score ([streams][ceil(N / kSampleStride)]), which the streamed selection samples
+// instead of F; it only places the bracket, so the kept sets do not depend on it.
+hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard,
+                         const float *samp, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
 // selection and compaction in one kernel (tria_prune) for the shapes where select_compact_fused holds
 bool select_compact_fused(int N, int B);
 hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, int N, int B, int32_t *kept,
-                                 const int *guard, void *k, void *v, int32_t *pos, hipStream_t st);
+                                 const int *guard, const float *samp, void *k, void *v, int32_t *pos,
+                                 hipStream_t st);
 
 }  // namespace tria

@@ -240,6 +240,22 @@ def test_scores_are_deterministic(T):
         assert np.array_equal(F1.view(np.uint32), F2.view(np.uint32))
 
 
+def test_config5_default_workspace_is_small(T):
+    """The prune step's workspace at Qwen3-32B (64 layers, 8 KV heads of 8 queries), 8 sequences
+    of 32768 bf16 keys: the default path reserves the matrix-core operands, pivots, the cluster
+    exchange and the side sample only (about 68 MB), not the raw scores that only the tiled path
+    stages (4.3 GB)."""
+    cfg = synth.CONFIGS[5]
+    Hq, L = cfg.n_q_heads, cfg.n_layers
+    rng = np.random.default_rng(5)
+    calib = T.load_calib(rng.standard_normal((L, Hq, 128), dtype=np.float32),
+                         np.ones((L, Hq, 64), np.float32), np.full((L, Hq, 64), 0.5, np.float32), cfg.n_kv_heads)
+    ws = T.prune_workspace_bytes(calib, cfg.n_seq, cfg.n_keys, cfg.budget)
+    assert 0 < ws < 100_000_000, ws
+    raw = cfg.n_seq * L * Hq * cfg.n_keys * 4
+    assert T.prune_workspace_bytes(calib, cfg.n_seq, cfg.n_keys, cfg.budget, flags=T.SCORE_TILED) > raw
+
+
 def test_prune_entry_point_matches_separate_calls(T):
     import torch
     cfg = variant(2, name="prune", n_seq=2, seed=39)
