@@ -29,10 +29,14 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
     const size_t streams = (size_t)n_seq * c->L * c->Hkv;
     const size_t heads = streams * c->G;
     const size_t fused_lds = (size_t)c->G * (size_t)N * 4 + (size_t)c->G * 192 * 4;
-    const bool perkey = (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0;
-    const bool mfma = dt == TRIA_BF16 && !perkey;          // the matrix-core operand prologue runs
     w.tiled = fused_lds > (size_t)kFusedLdsMax;
     w.tiles = (N + kTileKeys - 1) / kTileKeys;
+    // pre-RoPE bf16 keys too long for one block: turned to their positions inside the staged
+    // cluster kernel; the other per-key forms on the vector ALU
+    w.rot = dt == TRIA_BF16 && (flags & TRIA_KEYS_PRE_ROPE) && w.tiled &&
+            !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED | TRIA_TRIG_WEIGHT_R)) && stage_path_applies(c->G, N);
+    const bool perkey = (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0 && !w.rot;
+    const bool mfma = dt == TRIA_BF16 && !perkey;          // the matrix-core operand prologue runs
     w.cluster = mfma && w.tiled && !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED)) && cluster_path_applies(c->G, N);
     // raw scores staged in HBM: the per-key and offset-max kernels always, the other long streams
     // unless a stream cluster keeps them on chip
@@ -509,13 +513,14 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
                         const int32_t *t, int n_seq, int N, const float *qrot, float *F, float *raw,
                         float *stats, unsigned flags, const tria_score_ws &lay, char *ws, hipStream_t st)
 {
+    if (lay.rot) return launch_score_mfma(c, k, pos, t, n_seq, N, false, F, raw, stats, lay, ws, st);
     if (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE))
         return launch_score_perkey(c, dt, k, pos, t, n_seq, N, flags, F, raw, stats, lay, ws, st);
     const bool weight_r = (flags & TRIA_TRIG_WEIGHT_R) != 0;
     if (flags & TRIA_OFFSET_MAX) return launch_score_maxd(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
     // bf16 caches score on the matrix cores (their prologue rotates the queries itself); fp32
     // caches on the vector ALU, with the rotated queries from the workspace
-    if (dt == TRIA_BF16) return launch_score_mfma(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    if (dt == TRIA_BF16) return launch_score_mfma(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
     return launch_score_d<false>(c, k, n_seq, N, qrot, F, raw, stats, lay, ws, st);
 }
 

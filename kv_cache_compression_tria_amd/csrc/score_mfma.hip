@@ -68,10 +68,12 @@ __device__ __forceinline__ float bf16_term(float x, int b)
 // MFMA i (i < 4: trig K-block i; 4 + 2a + half: norm term a, band half).  The pivot of head h (the
 // fp32 score of the stream's first key) is a butterfly sum of the lanes' band terms (every lane
 // ends with the same bits).  Block 0 clears the error word and the blocks clear the stream
-// clusters' n_arrive arrival words.
-template <int G>
+// clusters' n_arrive arrival words.  ROT (pre-RoPE keys): the pivot's key is first turned to its
+// position (band f times exp(i w_f p), exact turn fraction, fp64 sincos).
+template <int G, bool ROT>
 __global__ __launch_bounds__(64) void prologue_kernel(const u32x4 *__restrict__ k, const double2 *__restrict__ P,
                                                       const uint64_t *__restrict__ nu, const int32_t *__restrict__ t,
+                                                      const int32_t *__restrict__ pos,
                                                       const float *__restrict__ R, const float *__restrict__ W, int L,
                                                       int Hkv, int N, u32x4 *__restrict__ ops, float *__restrict__ pivot,
                                                       int *__restrict__ err, uint32_t *__restrict__ arrive, int n_arrive)
@@ -124,8 +126,16 @@ __global__ __launch_bounds__(64) void prologue_kernel(const u32x4 *__restrict__ 
         }
     // pivots: lane f holds band f of the stream's first key
     const uint16_t *row = (const uint16_t *)(k + (size_t)sid * N * 16);
-    const float re = __uint_as_float((uint32_t)row[lane] << 16), im = __uint_as_float((uint32_t)row[TRIA_HALF + lane] << 16);
+    float re = __uint_as_float((uint32_t)row[lane] << 16), im = __uint_as_float((uint32_t)row[TRIA_HALF + lane] << 16);
     const float nrm = sqrtf(re * re + im * im);
+    if (ROT) {
+        const uint64_t turns = (uint64_t)(int64_t)pos[(size_t)sid * N] * nu[lane];
+        double sn, cs;
+        sincospi(2.0 * ((double)(int64_t)turns * 0x1p-64), &sn, &cs);
+        const float r2 = (float)(re * cs - im * sn), i2 = (float)(re * sn + im * cs);
+        re = r2;
+        im = i2;
+    }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         float x = fmaf(q[hh][lane], re, fmaf(q[hh][TRIA_HALF + lane], im, wrow[hh * TRIA_HALF + lane] * nrm));
@@ -136,13 +146,17 @@ __global__ __launch_bounds__(64) void prologue_kernel(const u32x4 *__restrict__ 
 }
 
 template <int G>
-static hipError_t launch_prologue(const tria_calib *c, const u32x4 *kp, const int32_t *t, int n_seq, int N,
-                                  bool weight_r, u32x4 *ops, float *pivot, int *err, uint32_t *arrive, int n_arrive,
-                                  hipStream_t st)
+static hipError_t launch_prologue(const tria_calib *c, const u32x4 *kp, const int32_t *t, const int32_t *pos, int n_seq,
+                                  int N, bool weight_r, u32x4 *ops, float *pivot, int *err, uint32_t *arrive,
+                                  int n_arrive, hipStream_t st)
 {
     const int streams = n_seq * c->L * c->Hkv;
-    prologue_kernel<G><<<streams, 64, 0, st>>>(kp, c->P, c->nu, t, weight_r ? c->R : nullptr, c->W, c->L, c->Hkv, N,
-                                               ops, pivot, err, arrive, n_arrive);
+    if (pos)
+        prologue_kernel<G, true><<<streams, 64, 0, st>>>(kp, c->P, c->nu, t, pos, weight_r ? c->R : nullptr, c->W,
+                                                         c->L, c->Hkv, N, ops, pivot, err, arrive, n_arrive);
+    else
+        prologue_kernel<G, false><<<streams, 64, 0, st>>>(kp, c->P, c->nu, t, nullptr, weight_r ? c->R : nullptr, c->W,
+                                                          c->L, c->Hkv, N, ops, pivot, err, arrive, n_arrive);
     return hipGetLastError();
 }
 
@@ -195,19 +209,12 @@ __device__ __forceinline__ float band_sq(uint32_t pair)
     return __builtin_amdgcn_fdot2_f32_bf16(p, p, 0.f, false);
 }
 
-// Scores of one 16-key tile: lane (g, j) returns v[0], v[1] = heads head_a(g), head_a(g) + 2 of
-// key j (zero for heads >= G).
-__device__ __forceinline__ void score_tile16(const u32x4 (&ka)[4], const Ops &c, float (&v)[2])
+// Band-norm contraction of one 16-key tile into acc: bands 8g+e (re in ka[0], im in ka[2]) and
+// 32+8g+e (re in ka[1], im in ka[3]); v_perm pairs (re, im) of a band, v_dot2 forms re^2 + im^2
+// from the bf16 halves in fp32, and the two-term split of a pair of norms costs two packed
+// conversions, a shift, a mask and two subtractions.
+__device__ __forceinline__ floatx4 norm_tile16(const u32x4 (&ka)[4], const Ops &c, floatx4 acc)
 {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[kb], __builtin_bit_cast(bf16x8, ka[kb]), acc, 0, 0, 0);
-
-    // band norms: bands 8g+e (re in ka[0], im in ka[2]) and 32+8g+e (re in ka[1], im in ka[3]);
-    // v_perm pairs (re, im) of a band, v_dot2 forms re^2 + im^2 from the bf16 halves in fp32,
-    // and the two-term split of a pair of norms costs two packed conversions, a shift, a mask
-    // and two subtractions
     u32x4 t0[2], t1[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -230,13 +237,84 @@ __device__ __forceinline__ void score_tile16(const u32x4 (&ka)[4], const Ops &c,
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[0][half], __builtin_bit_cast(bf16x8, t0[half]), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[1][half], __builtin_bit_cast(bf16x8, t1[half]), acc, 0, 0, 0);
     }
+    return acc;
+}
 
-    // lanes l < 32 hold term 0 of channels 4g + r, lanes l + 32 term 1 of the same heads
+// lanes l < 32 hold term 0 of channels 4g + r, lanes l + 32 term 1 of the same heads: one swap per
+// pair of accumulator registers adds them up
+__device__ __forceinline__ void combine_terms(floatx4 acc, float (&v)[2])
+{
     float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
     permlane32_swap(a0, a1);
     permlane32_swap(a2, a3);
     v[0] = a0 + a1;
     v[1] = a2 + a3;
+}
+
+// Scores of one 16-key tile: lane (g, j) returns v[0], v[1] = heads head_a(g), head_a(g) + 2 of
+// key j (zero for heads >= G).
+__device__ __forceinline__ void score_tile16(const u32x4 (&ka)[4], const Ops &c, float (&v)[2])
+{
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[kb], __builtin_bit_cast(bf16x8, ka[kb]), acc, 0, 0, 0);
+    combine_terms(norm_tile16(ka, c, acc), v);
+}
+
+// The same for pre-RoPE keys, which lane (g, j) first turns to key j's position p (RoPE applied on
+// the fly): band f (re = dim f, im = dim f + 64) times exp(i w_f p).  The angle in turns is the
+// top 32 bits of p nu_f mod 2^64, exact for any 32-bit p from two 32-bit products: with
+// nu_f = hi 2^32 + lo and lo read as a signed word s (lo = s + 2^32 [lo >= 2^31]), the top word is
+// p (hi + [lo >= 2^31]) + mulhi_signed(p, s) mod 2^32; nu_l holds (s, hi + [lo >= 2^31]) per band.
+// The hardware sine and cosine take the angle in turns.  The turned key is no longer exact in
+// bf16, so it enters as two bf16 terms (x = x0 + x1, |x - x0 - x1| <= 2^-18 |x|): eight
+// trigonometric MFMAs instead of four.  The band norms do not change under the turn and come from
+// the loaded key.
+__device__ __forceinline__ void score_tile16_rot(const u32x4 (&ka)[4], const Ops &c, int32_t p,
+                                                 const int2 *__restrict__ nu_l, float (&v)[2])
+{
+    const int grp = (threadIdx.x & 63) >> 4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const u32x4 x = ka[half], y = ka[2 + half];
+        u32x4 rh, rl, ih, il;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f = 32 * half + 8 * grp + 2 * i;
+            const int4 nn = *(const int4 *)&nu_l[f];     // bands f and f + 1
+            const float re[2] = {__uint_as_float(x[i] << 16), __uint_as_float(x[i] & 0xffff0000u)};
+            const float im[2] = {__uint_as_float(y[i] << 16), __uint_as_float(y[i] & 0xffff0000u)};
+            float r[2], q[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int s_lo = e ? nn.z : nn.x, hi = e ? nn.w : nn.y;
+                const uint32_t top = (uint32_t)p * (uint32_t)hi + (uint32_t)__mulhi(p, s_lo);
+                const float a = (float)(int32_t)top * 0x1p-32f;
+                const float sn = __builtin_amdgcn_sinf(a), cs = __builtin_amdgcn_cosf(a);
+                r[e] = fmaf(re[e], cs, -im[e] * sn);
+                q[e] = fmaf(re[e], sn, im[e] * cs);
+            }
+            const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r[0], r[1]}, bf16x2));
+            const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{q[0], q[1]}, bf16x2));
+            rh[i] = h0;
+            ih[i] = h1;
+            rl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                     float2v{r[0] - __uint_as_float(h0 << 16),
+                                                             r[1] - __uint_as_float(h0 & 0xffff0000u)},
+                                                     bf16x2));
+            il[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                     float2v{q[0] - __uint_as_float(h1 << 16),
+                                                             q[1] - __uint_as_float(h1 & 0xffff0000u)},
+                                                     bf16x2));
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[half], __builtin_bit_cast(bf16x8, rh), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[half], __builtin_bit_cast(bf16x8, rl), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[2 + half], __builtin_bit_cast(bf16x8, ih), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[2 + half], __builtin_bit_cast(bf16x8, il), acc, 0, 0, 0);
+    }
+    combine_terms(norm_tile16(ka, c, acc), v);
 }
 
 // Moments of one head around the stream pivot P: S1 = sum (v - P), S2 = sum (v - P)^2 (fp64),
@@ -371,6 +449,16 @@ struct WaveScorer {
     __device__ void score(const u32x4 (&b)[4], int nvalid, float (&v)[2])
     {
         score_tile16(b, c, v);
+        add(nvalid, v);
+    }
+    // the same for a tile of pre-RoPE keys, turned to their positions (lane's key at position p)
+    __device__ void score_rot(const u32x4 (&b)[4], int32_t p, const int2 *nu_l, int nvalid, float (&v)[2])
+    {
+        score_tile16_rot(b, c, p, nu_l, v);
+        add(nvalid, v);
+    }
+    __device__ __forceinline__ void add(int nvalid, const float (&v)[2])
+    {
         const int lane = threadIdx.x & 63;
         const int j = lane & 15, ha = head_a(lane >> 4);
         const bool ok = j < nvalid;
@@ -915,14 +1003,26 @@ constexpr int stage_full_items()
     return ((kmax + 15) / 16 + kClusterWaves - 1) / kClusterWaves;
 }
 
+// one 4-byte-per-lane memory-to-LDS load: lane l's word at `src` lands at lds_base + 4 l
+__device__ __forceinline__ void dma4(const int32_t *src, const int32_t *lds_base)
+{
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(src), "s"(la)
+                 : "memory", "m0");
+}
+
 // NTC > 0: every block of the launch runs exactly NTC items per wave and round (known at compile
 // time, so that the item and round indices are shifts and masks, not divisions); 0: any count.
-template <int G, int NTC>
+// ROT: the keys are cached before RoPE; each tile's positions (pos) come into LDS with its rows,
+// and the keys are turned to them before the contraction (score_tile16_rot, band turn fractions
+// nu).  Every tile is then five loads per wave instead of four.
+template <int G, int NTC, bool ROT>
 __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ ops, const float *__restrict__ pivot, int N,
     int streams, int Ps, int Kb, int cpx, int C, double *__restrict__ xpart, uint32_t *__restrict__ arrive,
     float *__restrict__ F, float *__restrict__ samp, float *__restrict__ raw_out, float *__restrict__ stats,
-    int *__restrict__ err)
+    int *__restrict__ err, const int32_t *__restrict__ pos, const uint64_t *__restrict__ nu)
 {
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
@@ -939,6 +1039,8 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     __shared__ uint32_t flg[64];                   // the cluster's arrival flags, fetched by wave 0
     __shared__ float pvs[2][8];                    // pivots of the streams of rounds r and r + 1
     __shared__ uint32_t zstamp;                    // rounds whose mean and 1/std are in zmu, zinv
+    __shared__ int32_t pslot[NW][2][ROT ? 64 : 1]; // ROT: positions of each slot's tile (row l & 15 at l)
+    __shared__ __attribute__((aligned(16))) int2 nu_l[ROT ? TRIA_HALF : 1];   // ROT: per band, see score_tile16_rot
     static_assert(NW == kOps, "one 1 KB operand load per wave");
     const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
     const int cl = x * cpx + y / Ps, part = y % Ps;
@@ -972,6 +1074,14 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
     hold(__builtin_bit_cast(uint32_t, ws.p[1]));
     if (wid == 0 && lane < G) pvs[0][lane] = pivot[(size_t)cl * G + lane];
     if (threadIdx.x == 0) zstamp = 0;     // read by the other waves only after the first barrier
+    if constexpr (ROT) {
+        if (threadIdx.x < TRIA_HALF) {
+            const uint64_t v = nu[threadIdx.x];
+            const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32) + (lo >> 31);
+            nu_l[threadIdx.x] = make_int2((int)lo, (int)hi);
+        }
+        __syncthreads();
+    }
 
     // Item li of a round is tile tile_of(li) of the block's part: wid + NW li, or, when the item
     // count is a known even number, the pairs 2 NW (li / 2) + 2 wid + (li & 1), so that every
@@ -996,19 +1106,37 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
             const int row = 4 * m + (lane >> 4);
             dma16(base + (row < valid ? row : 0) * 16 + ((lane & 15) ^ row), slot + 64 * m);
         }
+        if constexpr (ROT) {
+            // the rows' positions: lane l takes row l & 15 (rows at or past valid: row 0)
+            const int row = lane & 15;
+            const int32_t *pb = t >= 0 ? pos + (size_t)sid * N + prt(r) * Kb + t * 16 : pos + (size_t)sid * N;
+            dma4(pb + (row < valid ? row : 0), &pslot[wid][i & 1][0]);
+        }
     };
     // Wait until every vector memory operation but the newest 4 + e has completed: the newest
     // tile's 4 loads and the e operations (all written out in this kernel, so their count is
     // exact) that followed them.  Operations complete in issue order for this count, so a load
     // or store issued just after a tile is next waited for together with the following tile.
+    // (ROT: the newest tile's 5 loads)
     auto wait_ring = [&](int e) {
-        switch (e) {
-        case 0: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-        case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        if constexpr (ROT) {
+            switch (e) {
+            case 0: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+            case 1: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+            case 2: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+            case 3: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+            case 4: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+            }
+        } else {
+            switch (e) {
+            case 0: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+            case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+            case 2: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+            case 3: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+            case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+            }
         }
     };
     // the operand words (1 KB per wave) and pivots of the stream of round rn, loaded into LDS buffer
@@ -1074,13 +1202,17 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         wait_ring(e_prev);
         u32x4 b[4];
         read_item(i, b);
+        const int32_t kpos = ROT ? pslot[wid][i & 1][jj] : 0;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot has been read
         load_item(i + 2);
         int e = 0;
         if (rn_ops >= 0) e += stage_ops(rn_ops);
         if (pub_r >= 0) e += publish(pub_r);
         if (cnt >= 0) e += count_arrival(cnt);
-        ws.score(b, nkr - tile_of(li) * 16, v);
+        if constexpr (ROT)
+            ws.score_rot(b, kpos, nu_l, nkr - tile_of(li) * 16, v);
+        else
+            ws.score(b, nkr - tile_of(li) * 16, v);
         return e;
     };
     // ---- finishing round r: the cluster's partial sums -> mean and 1/std per head -> F
@@ -1218,9 +1350,10 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 #pragma unroll
                 for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[key * GP + h] - zmu[h]) * zinv[h]);
                 __builtin_nontemporal_store(z, &fo[key]);   // read back by the selection, not now
-                // the first key of each 16-key tile (jr is a multiple of 16) to the side sample
+                // the first key of each 16-key tile (jr is a multiple of 16) to the side sample;
+                // a plain store, so that L2 merges a line's 16 samples before it is written back
                 static_assert(kSampleStride == 16, "one sampled key per 16-key tile");
-                if ((idx & 15) == 0) __builtin_nontemporal_store(z, &so[key >> 4]);
+                if ((idx & 15) == 0) so[key >> 4] = z;
                 if (raw_out)
 #pragma unroll
                     for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + jr + key] = lraw[key * GP + h];
@@ -1374,7 +1507,7 @@ static bool stage_plan(int N, ClusterPlan &pl)
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
         return false;
     if (!coop || n_cu <= 0) return false;
-    if (allow_dynamic_lds((const void *)score_mfma_stage_kernel<G, 0>, kStageLds) != hipSuccess) return false;
+    if (allow_dynamic_lds((const void *)score_mfma_stage_kernel<G, 0, false>, kStageLds) != hipSuccess) return false;
     const int kmax = (kStageLds / (GP * 4)) & ~15;
     int Ps = 1;
     while ((long long)Ps * kmax < N) Ps *= 2;
@@ -1383,7 +1516,7 @@ static bool stage_plan(int N, ClusterPlan &pl)
     const int nb = (n_cu / (8 * Ps)) * 8 * Ps;
     if (nb <= 0 || nb > kClusterMaxBlocks) return false;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_stage_kernel<G, 0>, NW * 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_stage_kernel<G, 0, false>, NW * 64,
                                                      (size_t)Kb * GP * 4) != hipSuccess || per_cu < 1)
         return false;
     pl.Ps = Ps;
@@ -1421,10 +1554,12 @@ static bool cached_plan(bool staged, int N, ClusterPlan &pl)
     return ok;
 }
 
+// rot: pre-RoPE keys at positions pos (band turn fractions nu)
 template <int G>
 static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u32x4 *ops, const float *pivot,
                                  int N, int streams, float *F, float *raw_out, float *stats,
-                                 const tria_score_ws &lay, char *ws, hipStream_t st)
+                                 const tria_score_ws &lay, char *ws, const int32_t *pos, const uint64_t *nu,
+                                 bool rot, hipStream_t st)
 {
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
@@ -1437,14 +1572,18 @@ static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u
     void *args[] = {(void *)&kp,    (void *)&ops,   (void *)&pivot, &n,
                     &S,             &Ps,            &Kb,            &cpx,
                     &C,             (void *)&xpart, (void *)&arrive, (void *)&F,
-                    (void *)&samp,  (void *)&raw_out, (void *)&stats, (void *)&err};
+                    (void *)&samp,  (void *)&raw_out, (void *)&stats, (void *)&err,
+                    (void *)&pos,   (void *)&nu};
     // every block full (the first and the last part of a stream run the same item count): the
     // variant with that count built in
     auto items = [](int nkeys) { return std::max(1, ((nkeys + 15) / 16 + NW - 1) / NW); };
     constexpr int full = stage_full_items<G>();
     const bool exact = items(pl.Kb) == full && items(N - (pl.Ps - 1) * pl.Kb) == full;
-    const void *fn = exact ? (const void *)score_mfma_stage_kernel<G, full> : (const void *)score_mfma_stage_kernel<G, 0>;
-    if (exact && allow_dynamic_lds(fn, kStageLds) != hipSuccess) return hipErrorInvalidValue;
+    const void *fn = rot ? (exact ? (const void *)score_mfma_stage_kernel<G, full, true>
+                                  : (const void *)score_mfma_stage_kernel<G, 0, true>)
+                         : (exact ? (const void *)score_mfma_stage_kernel<G, full, false>
+                                  : (const void *)score_mfma_stage_kernel<G, 0, false>);
+    if ((exact || rot) && allow_dynamic_lds(fn, kStageLds) != hipSuccess) return hipErrorInvalidValue;
     KernelTimer timer(TRIA_TIMER_SCORE_KEYS, st);
     return hipLaunchCooperativeKernel(fn, dim3(pl.nb), dim3(NW * 64), args, (unsigned)lds, st);
 }
@@ -1663,7 +1802,7 @@ static hipError_t launch_maxd_g(const tria_calib *c, const void *k, const int32_
     u32x4 *ops = (u32x4 *)(ws + lay.ops_off);
     float *pivot = (float *)(ws + lay.pivot_off);
     // the norm operands (the trigonometric ones are built per offset by the kernel, R-weighted there)
-    hipError_t e = launch_prologue<G>(c, kp, t, n_seq, N, false, ops, pivot, (int *)(ws + lay.err_off), nullptr, 0, st);
+    hipError_t e = launch_prologue<G>(c, kp, t, nullptr, n_seq, N, false, ops, pivot, (int *)(ws + lay.err_off), nullptr, 0, st);
     if (e != hipSuccess) return e;
     e = allow_dynamic_lds((const void *)score_maxd_kernel<G>, kMaxdOffsets * 4 * 64 * 16);
     if (e != hipSuccess) return e;
@@ -1736,8 +1875,9 @@ hipError_t launch_tile_finish(int G, int streams, int N, int tiles, const float 
 }
 
 template <int G>
-static hipError_t launch_mfma_g(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
-                                float *F, float *raw_out, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+static hipError_t launch_mfma_g(const tria_calib *c, const void *k, const int32_t *pos, const int32_t *t, int n_seq,
+                                int N, bool weight_r, float *F, float *raw_out, float *stats, const tria_score_ws &lay,
+                                char *ws, hipStream_t st)
 {
     const int streams = n_seq * c->L * c->Hkv;
     int *err = (int *)(ws + lay.err_off);
@@ -1759,9 +1899,12 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, const int32_
     }
     // the cluster paths' arrival words (one flag per block, or one counter per cluster) are cleared
     // by the prologue
+    // pre-RoPE keys are turned inside the staged kernel only (the layout planned it)
+    if (lay.rot && (path != kStaged || !pos)) return hipErrorInvalidValue;
     uint32_t *arrive = (path == kStaged || path == kRing) ? (uint32_t *)(ws + lay.arrive_off) : nullptr;
     const int n_arrive = path == kStaged ? pl.nb : path == kRing ? pl.C : 0;
-    hipError_t e = launch_prologue<G>(c, kp, t, n_seq, N, weight_r, ops, pivot, err, arrive, n_arrive, st);
+    hipError_t e = launch_prologue<G>(c, kp, t, lay.rot ? pos : nullptr, n_seq, N, weight_r, ops, pivot, err, arrive,
+                                      n_arrive, st);
     if (e != hipSuccess) return e;
     if (path == kOnChip) {
         const size_t lds = (size_t)G * (N | 1) * 4;
@@ -1771,7 +1914,9 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, const int32_
         score_mfma_fused_kernel<G><<<streams, kScoreThreads, lds, st>>>(kp, ops, pivot, N, F, raw_out, stats, err);
         return hipGetLastError();
     }
-    if (path == kStaged) return launch_stage_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
+    if (path == kStaged)
+        return launch_stage_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, pos, c->nu, lay.rot != 0,
+                                 st);
     if (path == kRing) return launch_cluster_g<G>(pl, kp, ops, pivot, N, streams, F, raw_out, stats, lay, ws, st);
     // raw scores go straight into the caller's raw output when there is one (same layout)
     float *raw = raw_out ? raw_out : (float *)(ws + lay.raw_off);
@@ -1794,6 +1939,28 @@ static bool cluster_applies_g(int N)
     return cached_plan<G>(true, N, pl) || cached_plan<G>(false, N, pl);
 }
 
+template <int G>
+static bool stage_applies_g(int N)
+{
+    ClusterPlan pl;
+    return cached_plan<G>(true, N, pl);
+}
+
+bool stage_path_applies(int G, int N)
+{
+    switch (G) {
+    case 1: return stage_applies_g<1>(N);
+    case 2: return stage_applies_g<2>(N);
+    case 3: return stage_applies_g<3>(N);
+    case 4: return stage_applies_g<4>(N);
+    case 5: return stage_applies_g<5>(N);
+    case 6: return stage_applies_g<6>(N);
+    case 7: return stage_applies_g<7>(N);
+    case 8: return stage_applies_g<8>(N);
+    }
+    return false;
+}
+
 bool cluster_path_applies(int G, int N)
 {
     switch (G) {
@@ -1809,18 +1976,19 @@ bool cluster_path_applies(int G, int N)
     return false;
 }
 
-hipError_t launch_score_mfma(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
-                             float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st)
+hipError_t launch_score_mfma(const tria_calib *c, const void *k, const int32_t *pos, const int32_t *t, int n_seq,
+                             int N, bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay,
+                             char *ws, hipStream_t st)
 {
     switch (c->G) {
-    case 1: return launch_mfma_g<1>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 2: return launch_mfma_g<2>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 3: return launch_mfma_g<3>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 4: return launch_mfma_g<4>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 5: return launch_mfma_g<5>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 6: return launch_mfma_g<6>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 7: return launch_mfma_g<7>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
-    case 8: return launch_mfma_g<8>(c, k, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 1: return launch_mfma_g<1>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 2: return launch_mfma_g<2>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 3: return launch_mfma_g<3>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 4: return launch_mfma_g<4>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 5: return launch_mfma_g<5>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 6: return launch_mfma_g<6>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 7: return launch_mfma_g<7>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
+    case 8: return launch_mfma_g<8>(c, k, pos, t, n_seq, N, weight_r, F, raw, stats, lay, ws, st);
     }
     return hipErrorInvalidValue;
 }

@@ -36,6 +36,7 @@ struct tria_score_ws {
     int tiles;       // key tiles (blocks) per stream on the tiled path
     int cluster;     // 1: long bf16 streams are scored by stream clusters (xpart, arrive, samp reserved)
     int has_raw;     // 1: raw scores, tile partials and per-head mean / 1/std are reserved
+    int rot;         // 1: pre-RoPE bf16 keys, turned to their positions inside the staged cluster kernel
 };
 
 namespace tria {
@@ -76,6 +77,7 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
 // True when bf16 streams of n_keys keys at group size G can be scored by stream clusters on the
 // current device (cooperative launch, clusters of at most 32 blocks).
 bool cluster_path_applies(int G, int n_keys);
+bool stage_path_applies(int G, int n_keys);   // the staged cluster kernel (one of the two above)
 
 // Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once per (kernel, device);
 // thread-safe.
@@ -90,8 +92,10 @@ hipError_t launch_score(const tria_calib *c, tria_dtype dt, const void *k, const
 int mfma_ops_per_stream(int G);   // 16-byte operand words per lane and stream (prologue output)
 // bf16 keys on the matrix cores: a prologue kernel rotates the queries (t, R-weighted with weight_r),
 // builds the operands and pivots and clears the error word, then the scoring kernels run
-hipError_t launch_score_mfma(const tria_calib *c, const void *k, const int32_t *t, int n_seq, int N, bool weight_r,
-                             float *F, float *raw, float *stats, const tria_score_ws &lay, char *ws, hipStream_t st);
+// pos: key positions, read when lay.rot (pre-RoPE keys turned to their positions on the staged path)
+hipError_t launch_score_mfma(const tria_calib *c, const void *k, const int32_t *pos, const int32_t *t, int n_seq,
+                             int N, bool weight_r, float *F, float *raw, float *stats, const tria_score_ws &lay,
+                             char *ws, hipStream_t st);
 // per-head statistics and z-max of the tiled paths over raw [streams][G][N] and the tile partials
 // part [streams][tiles][G][4] (sums around pivot[stream][h], or around 0 when pivot is null)
 hipError_t launch_tile_finish(int G, int streams, int N, int tiles, const float *raw, const double *part,

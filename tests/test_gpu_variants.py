@@ -77,6 +77,58 @@ def test_per_key_phase_agrees_with_default_path(T):
     calib.free()
 
 
+# ---- pre-RoPE keys on the matrix cores (streams long enough for the staged stream clusters) -------
+
+def _pre_rope_workspaces(T, calib, cfg):
+    """The matrix-core path stages no raw scores; the vector path (forced by the tiled flag) does."""
+    mfma = T.score_workspace_bytes(calib, cfg.n_seq, cfg.n_keys, flags=T.KEYS_PRE_ROPE)
+    valu = T.score_workspace_bytes(calib, cfg.n_seq, cfg.n_keys, flags=T.KEYS_PRE_ROPE | T.SCORE_TILED)
+    return mfma, valu
+
+
+def test_pre_rope_matrix_cores_config5_shape(orc, T):
+    """Qwen3-32B heads (8 KV heads of 8 queries), 2 layers of one sequence, 32768 pre-RoPE keys per
+    stream at positions 0..32767: every stream against the oracle."""
+    cfg = gc.variant(5, name="pre-rope-c5-shape", n_layers=2, n_seq=1, seed=370)
+    out, _ = gc.run_case(orc, T, cfg, flags=T.KEYS_PRE_ROPE)
+    wl = synth.make_host(cfg, pre_rope=True)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    mfma, valu = _pre_rope_workspaces(T, calib, cfg)
+    assert mfma < valu // 4, (mfma, valu)
+    calib.free()
+
+
+@pytest.mark.parametrize("G,N,t", [(8, 5000, 2 ** 31 - 1), (4, 9000, 2 ** 31 - 7), (2, 20000, 1_000_003)])
+def test_pre_rope_matrix_cores_large_positions(orc, T, G, N, t):
+    """Positions drawn up to t (up to 2^31 - 1): the 32-bit turn fractions of every band (signed low
+    word, adjusted high word) must match the oracle's exact phases; ragged last tiles."""
+    cfg = gc.variant(2, name=f"pre-rope-g{G}-N{N}-t{t}", n_q_heads=2 * G, n_kv_heads=2, n_seq=2, n_keys=N,
+                     budget=N // 4 + 3, t_fixed=t, calib="head_r", r_range=(0.6, 0.99), seed=371 + G)
+    gc.run_case(orc, T, cfg, flags=T.KEYS_PRE_ROPE)
+
+
+def test_pre_rope_matrix_cores_agree_with_vector_alu(T):
+    """The same pre-RoPE cache scored on the matrix cores and on the vector ALU (the tiled flag
+    keeps long pre-RoPE streams there): final scores within 2e-4 relative (both are within 1e-4 of
+    the oracle), identical kept sets away from near-ties."""
+    import torch
+    cfg = gc.variant(5, name="pre-rope-c5-2way", n_layers=1, n_seq=1, n_keys=24000, budget=2500, seed=380,
+                     positions="gapped", t_fixed=60000)
+    wl = synth.make_host(cfg, pre_rope=True)
+    dev = synth.to_device(wl)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    mfma, valu = _pre_rope_workspaces(T, calib, cfg)
+    assert mfma < valu // 4, (mfma, valu)
+    F0 = T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=T.KEYS_PRE_ROPE, check=True)
+    F1 = T.score(calib, dev["k"], dev["t_dev"], pos=dev["pos"], flags=T.KEYS_PRE_ROPE | T.SCORE_TILED, check=True)
+    torch.cuda.synchronize()
+    a, b = F0.cpu().numpy().astype(np.float64), F1.cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(a - b) / np.maximum(np.abs(a), 1.0))
+    print(f"\n[ok] pre-RoPE matrix cores vs vector ALU: F err {err:.2e}", flush=True)
+    assert err <= 2e-4
+    calib.free()
+
+
 def test_variant_budget_one_and_single_key(orc, T):
     gc.run_case(orc, T, gc.variant(2, name="var-b1", n_q_heads=8, n_kv_heads=2, n_keys=300, budget=1, seed=341),
                 flags=T.KEYS_PRE_ROPE)
