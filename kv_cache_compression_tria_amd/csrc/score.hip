@@ -37,7 +37,11 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
             !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED | TRIA_TRIG_WEIGHT_R)) && stage_path_applies(c->G, N);
     const bool perkey = (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0 && !w.rot;
     const bool mfma = dt == TRIA_BF16 && !perkey;          // the matrix-core operand prologue runs
-    w.cluster = mfma && w.tiled && !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED)) && cluster_path_applies(c->G, N);
+    // long bf16 streams: stream clusters when the device offers them; streams that fit one block
+    // too when there are enough of them to fill the chip
+    const bool free_path = mfma && !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED));
+    w.cluster = free_path && (w.tiled ? cluster_path_applies(c->G, N)
+                                      : streams >= kStageShortStreams && stage_path_applies(c->G, N));
     // raw scores staged in HBM: the per-key and offset-max kernels always, the other long streams
     // unless a stream cluster keeps them on chip
     w.has_raw = perkey || (flags & TRIA_OFFSET_MAX) || (w.tiled && !w.cluster);

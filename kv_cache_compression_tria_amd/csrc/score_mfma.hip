@@ -1494,10 +1494,18 @@ static hipError_t launch_cluster_g(const ClusterPlan &pl, const u32x4 *kp, const
                                       args, (unsigned)lds, st);
 }
 
-// Geometry of the staged cluster path (raw scores of at most kStageLds bytes per block); false
-// when it does not apply.
+// Geometry of the staged cluster path (raw scores of at most kStageLds bytes per block) for
+// `streams` streams of N keys; false when it does not apply.  Of the part counts Ps that fit
+// (Ps Kb >= N, Ps <= 32, parts of at least kStageMinKeys keys unless one part holds the stream),
+// the one with the least modelled time: rounds = ceil(streams / C) of Kb keys each, plus a fixed
+// cost per round worth kStageRoundKeys keys (the finish and the exchange).  Long streams take the
+// fewest parts that fit; few streams of moderate length spread over more parts, so that the
+// clusters' rounds come out even.
+constexpr int kStageRoundKeys = 256;
+constexpr int kStageMinKeys = 512;
+
 template <int G>
-static bool stage_plan(int N, ClusterPlan &pl)
+static bool stage_plan(int N, int streams, ClusterPlan &pl)
 {
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
@@ -1509,12 +1517,27 @@ static bool stage_plan(int N, ClusterPlan &pl)
     if (!coop || n_cu <= 0) return false;
     if (allow_dynamic_lds((const void *)score_mfma_stage_kernel<G, 0, false>, kStageLds) != hipSuccess) return false;
     const int kmax = (kStageLds / (GP * 4)) & ~15;
-    int Ps = 1;
-    while ((long long)Ps * kmax < N) Ps *= 2;
-    if (Ps > 32) return false;
+    int Ps0 = 1;
+    while ((long long)Ps0 * kmax < N) Ps0 *= 2;
+    if (Ps0 > 32) return false;
+    int best = -1;
+    double best_cost = 0.0;
+    for (int Ps = Ps0; Ps <= 32; Ps *= 2) {
+        const int Kb = ((N + Ps - 1) / Ps + 15) & ~15;
+        if (Ps > Ps0 && Kb < kStageMinKeys) break;
+        const int nb = (n_cu / (8 * Ps)) * 8 * Ps;
+        if (nb <= 0 || nb > kClusterMaxBlocks) break;
+        const int C = nb / Ps;
+        const double cost = (double)((streams + C - 1) / C) * (double)(Kb + kStageRoundKeys);
+        if (best < 0 || cost < best_cost) {
+            best = Ps;
+            best_cost = cost;
+        }
+    }
+    if (best < 0) return false;
+    const int Ps = best;
     const int Kb = ((N + Ps - 1) / Ps + 15) & ~15;
     const int nb = (n_cu / (8 * Ps)) * 8 * Ps;
-    if (nb <= 0 || nb > kClusterMaxBlocks) return false;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)score_mfma_stage_kernel<G, 0, false>, NW * 64,
                                                      (size_t)Kb * GP * 4) != hipSuccess || per_cu < 1)
@@ -1529,15 +1552,16 @@ static bool stage_plan(int N, ClusterPlan &pl)
 
 // The plans above query the device (attributes, occupancy) and raise dynamic-LDS limits: host work
 // of several microseconds that the GPU would otherwise wait for at every call.  Each (device, path,
-// G, N) is planned once and remembered.
+// G, N, streams) is planned once and remembered (whether a path applies does not depend on the
+// stream count).
 template <int G>
-static bool cached_plan(bool staged, int N, ClusterPlan &pl)
+static bool cached_plan(bool staged, int N, int streams, ClusterPlan &pl)
 {
     static std::mutex mu;
-    static std::map<std::tuple<int, bool, int>, std::pair<bool, ClusterPlan>> memo;   // (device, staged, N)
+    static std::map<std::tuple<int, bool, int, int>, std::pair<bool, ClusterPlan>> memo;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
-    const auto key = std::make_tuple(dev, staged, N);
+    const auto key = std::make_tuple(dev, staged, N, staged ? streams : 1);
     {
         std::lock_guard<std::mutex> lock(mu);
         const auto it = memo.find(key);
@@ -1547,7 +1571,7 @@ static bool cached_plan(bool staged, int N, ClusterPlan &pl)
         }
     }
     ClusterPlan p{};
-    const bool ok = staged ? stage_plan<G>(N, p) : cluster_plan<G>(N, p);
+    const bool ok = staged ? stage_plan<G>(N, streams, p) : cluster_plan<G>(N, p);
     std::lock_guard<std::mutex> lock(mu);
     memo[key] = std::make_pair(ok, p);
     pl = p;
@@ -1887,15 +1911,14 @@ static hipError_t launch_mfma_g(const tria_calib *c, const void *k, const int32_
     // the path: one block per stream (on chip), staged or register-ring stream clusters, or tiled
     enum { kOnChip, kStaged, kRing, kTiled } path = kOnChip;
     ClusterPlan pl{};
-    if (lay.tiled) {
-        if (lay.cluster) {
-            if (cached_plan<G>(true, N, pl)) path = kStaged;
-            else if (cached_plan<G>(false, N, pl)) path = kRing;
-            else return hipErrorInvalidValue;   // the layout planned a cluster path the device no longer offers
-        } else {
-            if (!lay.has_raw) return hipErrorInvalidValue;
-            path = kTiled;
-        }
+    if (lay.cluster) {
+        // (streams short enough for one block take the staged clusters only; the layout checked)
+        if (cached_plan<G>(true, N, streams, pl)) path = kStaged;
+        else if (lay.tiled && cached_plan<G>(false, N, 1, pl)) path = kRing;
+        else return hipErrorInvalidValue;   // the layout planned a cluster path the device no longer offers
+    } else if (lay.tiled) {
+        if (!lay.has_raw) return hipErrorInvalidValue;
+        path = kTiled;
     }
     // the cluster paths' arrival words (one flag per block, or one counter per cluster) are cleared
     // by the prologue
@@ -1936,14 +1959,14 @@ template <int G>
 static bool cluster_applies_g(int N)
 {
     ClusterPlan pl;
-    return cached_plan<G>(true, N, pl) || cached_plan<G>(false, N, pl);
+    return cached_plan<G>(true, N, 1, pl) || cached_plan<G>(false, N, 1, pl);
 }
 
 template <int G>
 static bool stage_applies_g(int N)
 {
     ClusterPlan pl;
-    return cached_plan<G>(true, N, pl);
+    return cached_plan<G>(true, N, 1, pl);
 }
 
 bool stage_path_applies(int G, int N)

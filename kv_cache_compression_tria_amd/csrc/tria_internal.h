@@ -46,6 +46,7 @@ constexpr int kScoreThreads = 256;
 constexpr int kFusedLdsMax = 80 * 1024;   // raw scores of a stream kept on chip up to this size
 constexpr int kClusterLds = 128 * 1024;   // raw scores one block of a stream cluster keeps on chip
 constexpr int kClusterMaxBlocks = 1024;   // largest cluster grid the workspace has room for
+constexpr int kStageShortStreams = 256;   // streams that fit one block use the staged clusters from this many
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectStreamKeys = 32768;  // streams up to this many keys: the streamed selection (bitmaps of
                                           // 2 x N/32 words in LDS)
