@@ -1026,7 +1026,7 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
 {
     constexpr int NW = kClusterWaves;
     constexpr int GP = (G + 1) & ~1;
-    extern __shared__ float lraw[];                // [Kb][GP]
+    extern __shared__ __attribute__((aligned(16))) float lraw[];   // [Kb][GP]
     __shared__ u32x4 stg[NW][2][256];              // two 4 KB key-tile slots per wave
     __shared__ BlockSumsT<NW> bs;
     __shared__ float zmu[8], zinv[8];
@@ -1343,20 +1343,49 @@ __global__ __launch_bounds__(kClusterWaves * 64) void score_mfma_stage_kernel(
         const int jr = prt(r) * Kb, nkr = nk_of(r);
         float *fo = F + (size_t)sid * N + jr;
         float *so = samp + (size_t)sid * ((N + kSampleStride - 1) / kSampleStride) + jr / kSampleStride;
-        for (int idx = lane; idx < nt * 16; idx += 64) {
-            const int key = tile_of(idx >> 4) * 16 + (idx & 15);
-            if (key < nkr) {
-                float z = -INFINITY;
+        // a key's raw scores (GP floats from LDS; keys at or past nkr read key 0, not stored)
+        auto read_raw = [&](int key, float (&x)[GP]) {
+            const float2 *src = (const float2 *)(lraw + (key < nkr ? key : 0) * GP);
 #pragma unroll
-                for (int h = 0; h < G; ++h) z = fmaxf(z, (lraw[key * GP + h] - zmu[h]) * zinv[h]);
-                __builtin_nontemporal_store(z, &fo[key]);   // read back by the selection, not now
-                // the first key of each 16-key tile (jr is a multiple of 16) to the side sample;
-                // a plain store, so that L2 merges a line's 16 samples before it is written back
-                static_assert(kSampleStride == 16, "one sampled key per 16-key tile");
-                if ((idx & 15) == 0) so[key >> 4] = z;
-                if (raw_out)
+            for (int h2 = 0; h2 < GP / 2; ++h2) {
+                const float2 t = src[h2];
+                x[2 * h2] = t.x;
+                x[2 * h2 + 1] = t.y;
+            }
+        };
+        auto emit = [&](int idx, int key, const float (&x)[GP]) {
+            if (key >= nkr) return;
+            float z = -INFINITY;
 #pragma unroll
-                    for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + jr + key] = lraw[key * GP + h];
+            for (int h = 0; h < G; ++h) z = fmaxf(z, (x[h] - zmu[h]) * zinv[h]);
+            __builtin_nontemporal_store(z, &fo[key]);   // read back by the selection, not now
+            // the first key of each 16-key tile (jr is a multiple of 16) to the side sample;
+            // a plain store, so that L2 merges a line's 16 samples before it is written back
+            static_assert(kSampleStride == 16, "one sampled key per 16-key tile");
+            if ((idx & 15) == 0) so[key >> 4] = z;
+            if (raw_out)
+#pragma unroll
+                for (int h = 0; h < G; ++h) raw_out[((size_t)sid * G + h) * N + jr + key] = x[h];
+        };
+        if constexpr (NTC > 0 && NTC % 8 == 0 && GP == 8) {
+            // NTC * 16 / 64 keys per lane, two at a time with both keys' reads issued together, so
+            // that one LDS round trip serves two keys (not unrolled further: registers)
+#pragma unroll 1
+            for (int q = 0; q < NTC / 4; q += 2) {
+                const int i0 = lane + 64 * q, i1 = i0 + 64;
+                const int k0 = tile_of(i0 >> 4) * 16 + (i0 & 15), k1 = tile_of(i1 >> 4) * 16 + (i1 & 15);
+                float x0[GP], x1[GP];
+                read_raw(k0, x0);
+                read_raw(k1, x1);
+                emit(i0, k0, x0);
+                emit(i1, k1, x1);
+            }
+        } else {
+            for (int idx = lane; idx < nt * 16; idx += 64) {
+                const int key = tile_of(idx >> 4) * 16 + (idx & 15);
+                float x[GP];
+                read_raw(key, x);
+                emit(idx, key, x);
             }
         }
     };
@@ -1602,7 +1631,9 @@ static hipError_t launch_stage_g(const ClusterPlan &pl, const u32x4 *kp, const u
     // variant with that count built in
     auto items = [](int nkeys) { return std::max(1, ((nkeys + 15) / 16 + NW - 1) / NW); };
     constexpr int full = stage_full_items<G>();
-    const bool exact = items(pl.Kb) == full && items(N - (pl.Ps - 1) * pl.Kb) == full;
+    // (turned keys with G < 7: the built-in counts of 22 to 64 items spill ~90 registers, the
+    // variant with a runtime count none)
+    const bool exact = items(pl.Kb) == full && items(N - (pl.Ps - 1) * pl.Kb) == full && !(rot && G < 7);
     const void *fn = rot ? (exact ? (const void *)score_mfma_stage_kernel<G, full, true>
                                   : (const void *)score_mfma_stage_kernel<G, 0, true>)
                          : (exact ? (const void *)score_mfma_stage_kernel<G, full, false>
