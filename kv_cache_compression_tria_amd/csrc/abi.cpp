@@ -252,7 +252,8 @@ tria_status tria_score(const tria_calib *c, tria_dtype dt, const void *k, const 
     // bf16 keys on the matrix cores rotate the queries in their own prologue kernel; the other paths
     // get them from the rotation kernel.  Both clear the error word first (no memset node: safe
     // under graph capture).
-    const bool mfma = dt == TRIA_BF16 && !(flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE));
+    // (pre-RoPE bf16 keys on the staged clusters, lay.rot, take the prologue too)
+    const bool mfma = dt == TRIA_BF16 && (lay.rot || !(flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)));
     float *qrot = mfma ? nullptr : (float *)(w + lay.qrot_off);
     if (!mfma && tria::launch_rotate(c, t, n_seq, qrot, (int *)(w + lay.err_off), (flags & TRIA_TRIG_WEIGHT_R) != 0,
                                      st) != hipSuccess)
