@@ -972,7 +972,7 @@ __global__ __launch_bounds__(kSelectCompactThreads) void select_compact_kernel(c
     constexpr int NT = kSelectCompactThreads;
     select_stream_block<NT, kSelectSamples, 4>(blockIdx.x, F, N, B, kept, guard, samp);
     __syncthreads();   // the kept indices written by every thread are visible to the whole block
-    compact_stream<RV, NT, 2 * kCompactRows>(blockIdx.x, k, v, pos, kept, N, B);
+    compact_stream<RV, NT, kSelectCompactRows>(blockIdx.x, k, v, pos, kept, N, B);
 }
 
 __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N)
