@@ -959,7 +959,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
 // by them.  While some blocks of a CU select (bound by instruction issue and memory latency)
 // others move rows (bound by HBM bandwidth), and the kept indices are read back while they are
 // still in the caches.
-constexpr int kSelectCompactThreads = 512;
+constexpr int kSelectCompactThreads = 1024;
 
 template <int RV>
 __global__ __launch_bounds__(kSelectCompactThreads) void select_compact_kernel(const float *__restrict__ F, int N, int B,

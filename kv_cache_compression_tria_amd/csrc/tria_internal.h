@@ -53,7 +53,7 @@ constexpr int kSelectStreamKeys = 32768;  // streams up to this many keys: the s
 constexpr int kSampleStride = 16;     // the cluster scorers copy every 16th key's F to a side sample
 constexpr int kCompactThreads = 1024;   // the compaction kernel: one block of 16 waves per stream,
 constexpr int kCompactRows = 256;       // 256 rows per tile (few streams move faster with wide blocks)
-constexpr int kSelectCompactRows = 128; // rows per tile of the fused selection + compaction (512 threads)
+constexpr int kSelectCompactRows = 128; // rows per tile of the fused selection + compaction (1024 threads)
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
