@@ -240,6 +240,49 @@ def test_scores_are_deterministic(T):
         assert np.array_equal(F1.view(np.uint32), F2.view(np.uint32))
 
 
+@pytest.mark.parametrize("G,N,B", [(4, 17, 9), (4, 33, 20), (8, 100, 37), (4, 700, 500), (8, 700, 699)])
+def test_many_short_streams_on_the_staged_clusters(orc, T, G, N, B):
+    """512 streams that each fit one block take the staged stream clusters (256 or more streams),
+    with parts down to one 16-key tile per round and waves without a tile: every stream against
+    the oracle (raw and final scores, kept sets, selection, compaction)."""
+    pos_mode = "gapped" if N >= 256 else "contiguous"     # gapped draws keep the last 128 recent
+    cfg = variant(2, name=f"short-g{G}-N{N}", n_layers=32, n_seq=2, n_q_heads=8 * G, n_kv_heads=8,
+                  n_keys=N, budget=B, t_fixed=N + 3000, seed=400 + N + G, positions=pos_mode)
+    assert cfg.n_streams == 512
+    run_case(orc, T, cfg)
+    wl = synth.make_host(cfg)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    # the cluster exchange (2 x 1024 blocks x 8 heads x 4 doubles) is reserved: the staged path
+    # was planned; eight streams of the same length stay on chip and reserve none of it
+    assert T.score_workspace_bytes(calib, cfg.n_seq, N) > 512 * 1024
+    calib.free()
+    cfg8 = variant(2, name=f"short8-g{G}-N{N}", n_layers=1, n_seq=1, n_q_heads=8 * G, n_kv_heads=8,
+                   n_keys=N, budget=B, t_fixed=N + 3000, seed=401 + N + G, positions=pos_mode)
+    wl8 = synth.make_host(cfg8)
+    calib8 = T.load_calib(wl8["qc"], wl8["qn"], wl8["rb"], cfg8.n_kv_heads, cfg8.theta)
+    assert T.score_workspace_bytes(calib8, 1, N) < 512 * 1024
+    calib8.free()
+
+
+def test_many_single_key_streams_on_the_staged_clusters(T):
+    """512 one-key streams (staged clusters, one 16-key tile holding one key per part): every
+    head's spread is zero, so every final score is exactly 0, every stream keeps its key, and
+    the rows stay where they are."""
+    import torch
+    cfg = variant(2, name="single-512", n_layers=32, n_seq=2, n_q_heads=32, n_kv_heads=8, n_keys=1, budget=1,
+                  t_fixed=5000, seed=420, positions="contiguous")
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    k_before = dev["k"].clone()
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    F, kept = T.prune(calib, dev["k"], dev["v"], dev["pos"], dev["t_dev"], 1)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(F).item() == 0 and F.numel() == 512
+    assert torch.count_nonzero(kept).item() == 0 and kept.numel() == 512
+    assert torch.equal(dev["k"], k_before)
+    calib.free()
+
+
 def test_config5_default_workspace_is_small(T):
     """The prune step's workspace at Qwen3-32B (64 layers, 8 KV heads of 8 queries), 8 sequences
     of 32768 bf16 keys: the default path reserves the matrix-core operands, pivots, the cluster
