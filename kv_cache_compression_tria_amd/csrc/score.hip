@@ -31,9 +31,10 @@ tria_score_ws score_ws_layout(const tria_calib *c, tria_dtype dt, int n_seq, int
     const size_t fused_lds = (size_t)c->G * (size_t)N * 4 + (size_t)c->G * 192 * 4;
     w.tiled = fused_lds > (size_t)kFusedLdsMax;
     w.tiles = (N + kTileKeys - 1) / kTileKeys;
-    // pre-RoPE bf16 keys too long for one block: turned to their positions inside the staged
-    // cluster kernel; the other per-key forms on the vector ALU
-    w.rot = dt == TRIA_BF16 && (flags & TRIA_KEYS_PRE_ROPE) && w.tiled &&
+    // pre-RoPE bf16 keys on the staged clusters (streams too long for one block, or 256 or more
+    // streams): turned to their positions inside the kernel; the other per-key forms on the
+    // vector ALU
+    w.rot = dt == TRIA_BF16 && (flags & TRIA_KEYS_PRE_ROPE) && (w.tiled || streams >= kStageShortStreams) &&
             !(flags & (TRIA_OFFSET_MAX | TRIA_SCORE_TILED | TRIA_TRIG_WEIGHT_R)) && stage_path_applies(c->G, N);
     const bool perkey = (flags & (TRIA_PER_KEY_PHASE | TRIA_KEYS_PRE_ROPE)) != 0 && !w.rot;
     const bool mfma = dt == TRIA_BF16 && !perkey;          // the matrix-core operand prologue runs

@@ -107,6 +107,21 @@ def test_pre_rope_matrix_cores_large_positions(orc, T, G, N, t):
     gc.run_case(orc, T, cfg, flags=T.KEYS_PRE_ROPE)
 
 
+@pytest.mark.parametrize("G,N,B", [(4, 700, 500), (8, 2176, 2048)])
+def test_pre_rope_many_short_streams_on_the_matrix_cores(orc, T, G, N, B):
+    """512 pre-RoPE streams that each fit one block take the staged clusters with turned keys (the
+    workspace holds no raw scores): every stream against the oracle."""
+    cfg = gc.variant(2, name=f"pre-rope-short-g{G}-N{N}", n_layers=32, n_seq=2, n_q_heads=8 * G, n_kv_heads=8,
+                     n_keys=N, budget=B, t_fixed=N + 5000, seed=390 + G)
+    assert cfg.n_streams == 512
+    gc.run_case(orc, T, cfg, flags=T.KEYS_PRE_ROPE)
+    wl = synth.make_host(cfg, pre_rope=True)
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], cfg.n_kv_heads, cfg.theta)
+    mfma, valu = _pre_rope_workspaces(T, calib, cfg)
+    assert mfma < valu, (mfma, valu)
+    calib.free()
+
+
 def test_pre_rope_matrix_cores_agree_with_vector_alu(T):
     """The same pre-RoPE cache scored on the matrix cores and on the vector ALU (the tiled flag
     keeps long pre-RoPE streams there): final scores within 2e-4 relative (both are within 1e-4 of
