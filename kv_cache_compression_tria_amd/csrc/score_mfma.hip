@@ -209,10 +209,30 @@ __device__ __forceinline__ float band_sq(uint32_t pair)
     return __builtin_amdgcn_fdot2_f32_bf16(p, p, 0.f, false);
 }
 
+// Two-term bf16 split of a pair of fp32 values: hi = the pair rounded to bf16 (one packed
+// conversion), lo = the rounding errors x - hi, rounded to bf16 in turn (x = hi + lo to 2^-18 |x|).
+// x - bf16(x) is exact in fp32, so v_dot2 of the packed hi with (-1, 0) or (0, -1), added to x,
+// forms it with one rounding of an exact value: one instruction in place of the unpacking shift
+// or mask and the subtraction.  The (-1, 0) pair is held in a scalar register: written as a
+// constant, the compiler encodes it as the inline constant -1.0, which the hardware reads for this
+// operand as the fp32 pattern 0xbf800000, i.e. (0, -1).  The (0, -1) pair is that literal.
+struct Split2 {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float x0, float x1)
+{
+    uint32_t neg_lo;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(neg_lo));
+    const bf16x2 h = __builtin_convertvector(float2v{x0, x1}, bf16x2);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_lo), x0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, 0xbf800000u), x1, false);
+    return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r0, r1}, bf16x2))};
+}
+
 // Band-norm contraction of one 16-key tile into acc: bands 8g+e (re in ka[0], im in ka[2]) and
 // 32+8g+e (re in ka[1], im in ka[3]); v_perm pairs (re, im) of a band, v_dot2 forms re^2 + im^2
 // from the bf16 halves in fp32, and the two-term split of a pair of norms costs two packed
-// conversions, a shift, a mask and two subtractions.
+// conversions and two v_dot2.
 __device__ __forceinline__ floatx4 norm_tile16(const u32x4 (&ka)[4], const Ops &c, floatx4 acc)
 {
     u32x4 t0[2], t1[2];
@@ -223,13 +243,9 @@ __device__ __forceinline__ floatx4 norm_tile16(const u32x4 (&ka)[4], const Ops &
         for (int i = 0; i < 4; ++i) {
             const uint32_t p0 = __builtin_amdgcn_perm(y[i], x[i], 0x05040100u);
             const uint32_t p1 = __builtin_amdgcn_perm(y[i], x[i], 0x07060302u);
-            const float n0 = __builtin_amdgcn_sqrtf(band_sq(p0));
-            const float n1 = __builtin_amdgcn_sqrtf(band_sq(p1));
-            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{n0, n1}, bf16x2));
-            const float r0 = n0 - __builtin_bit_cast(float, hi << 16);
-            const float r1 = n1 - __builtin_bit_cast(float, hi & 0xffff0000u);
-            t0[half][i] = hi;
-            t1[half][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r0, r1}, bf16x2));
+            const Split2 n = split2(__builtin_amdgcn_sqrtf(band_sq(p0)), __builtin_amdgcn_sqrtf(band_sq(p1)));
+            t0[half][i] = n.hi;
+            t1[half][i] = n.lo;
         }
     }
 #pragma unroll
@@ -296,18 +312,11 @@ __device__ __forceinline__ void score_tile16_rot(const u32x4 (&ka)[4], const Ops
                 r[e] = fmaf(re[e], cs, -im[e] * sn);
                 q[e] = fmaf(re[e], sn, im[e] * cs);
             }
-            const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r[0], r[1]}, bf16x2));
-            const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{q[0], q[1]}, bf16x2));
-            rh[i] = h0;
-            ih[i] = h1;
-            rl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                                                     float2v{r[0] - __uint_as_float(h0 << 16),
-                                                             r[1] - __uint_as_float(h0 & 0xffff0000u)},
-                                                     bf16x2));
-            il[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                                                     float2v{q[0] - __uint_as_float(h1 << 16),
-                                                             q[1] - __uint_as_float(h1 & 0xffff0000u)},
-                                                     bf16x2));
+            const Split2 sr = split2(r[0], r[1]), sq = split2(q[0], q[1]);
+            rh[i] = sr.hi;
+            rl[i] = sr.lo;
+            ih[i] = sq.hi;
+            il[i] = sq.lo;
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[half], __builtin_bit_cast(bf16x8, rh), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[half], __builtin_bit_cast(bf16x8, rl), acc, 0, 0, 0);
@@ -1740,13 +1749,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_maxd_kernel(
             for (int q = 0; q < 4; ++q) {
                 const uint32_t p0 = __builtin_amdgcn_perm(y[q], x[q], 0x05040100u);
                 const uint32_t p1 = __builtin_amdgcn_perm(y[q], x[q], 0x07060302u);
-                const float n0 = __builtin_amdgcn_sqrtf(band_sq(p0));
-                const float n1 = __builtin_amdgcn_sqrtf(band_sq(p1));
-                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{n0, n1}, bf16x2));
-                const float r0 = n0 - __builtin_bit_cast(float, hi << 16);
-                const float r1 = n1 - __builtin_bit_cast(float, hi & 0xffff0000u);
-                t0[q] = hi;
-                t1[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r0, r1}, bf16x2));
+                const Split2 n = split2(__builtin_amdgcn_sqrtf(band_sq(p0)), __builtin_amdgcn_sqrtf(band_sq(p1)));
+                t0[q] = n.hi;
+                t1[q] = n.lo;
             }
             accn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[0][half], __builtin_bit_cast(bf16x8, t0), accn, 0, 0, 0);
             accn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[1][half], __builtin_bit_cast(bf16x8, t1), accn, 0, 0, 0);
