@@ -283,10 +283,12 @@ __device__ __forceinline__ void score_tile16(const u32x4 (&ka)[4], const Ops &c,
 // top 32 bits of p nu_f mod 2^64, exact for any 32-bit p from two 32-bit products: with
 // nu_f = hi 2^32 + lo and lo read as a signed word s (lo = s + 2^32 [lo >= 2^31]), the top word is
 // p (hi + [lo >= 2^31]) + mulhi_signed(p, s) mod 2^32; nu_l holds (s, hi + [lo >= 2^31]) per band.
-// The hardware sine and cosine take the angle in turns.  The turned key is no longer exact in
+// The hardware sine and cosine take the angle in turns; they get 1 + top / 2^32 with the fraction
+// truncated to 23 bits (angle error below 2^-23 turns).  The turned key is no longer exact in
 // bf16, so it enters as two bf16 terms (x = x0 + x1, |x - x0 - x1| <= 2^-18 |x|): eight
 // trigonometric MFMAs instead of four.  The band norms do not change under the turn and come from
-// the loaded key.
+// the loaded key: re^2 + im^2 from the unpacked halves (one product and one fused multiply-add,
+// exact products and one rounding, as v_dot2 forms it on the default path), in the same loop.
 __device__ __forceinline__ void score_tile16_rot(const u32x4 (&ka)[4], const Ops &c, int32_t p,
                                                  const int2 *__restrict__ nu_l, float (&v)[2])
 {
@@ -295,35 +297,42 @@ __device__ __forceinline__ void score_tile16_rot(const u32x4 (&ka)[4], const Ops
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const u32x4 x = ka[half], y = ka[2 + half];
-        u32x4 rh, rl, ih, il;
+        u32x4 rh, rl, ih, il, nh, nl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int f = 32 * half + 8 * grp + 2 * i;
             const int4 nn = *(const int4 *)&nu_l[f];     // bands f and f + 1
             const float re[2] = {__uint_as_float(x[i] << 16), __uint_as_float(x[i] & 0xffff0000u)};
             const float im[2] = {__uint_as_float(y[i] << 16), __uint_as_float(y[i] & 0xffff0000u)};
-            float r[2], q[2];
+            float r[2], q[2], nrm[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int s_lo = e ? nn.z : nn.x, hi = e ? nn.w : nn.y;
                 const uint32_t top = (uint32_t)p * (uint32_t)hi + (uint32_t)__mulhi(p, s_lo);
-                const float a = (float)(int32_t)top * 0x1p-32f;
+                // 1 + top / 2^32 built from the bits (v_alignbit: 0x3f800000 | top >> 9): the
+                // same angle modulo one turn, its fraction truncated to 23 bits
+                const float a = __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, top, 9));
                 const float sn = __builtin_amdgcn_sinf(a), cs = __builtin_amdgcn_cosf(a);
                 r[e] = fmaf(re[e], cs, -im[e] * sn);
                 q[e] = fmaf(re[e], sn, im[e] * cs);
+                nrm[e] = __builtin_amdgcn_sqrtf(fmaf(re[e], re[e], im[e] * im[e]));
             }
-            const Split2 sr = split2(r[0], r[1]), sq = split2(q[0], q[1]);
+            const Split2 sr = split2(r[0], r[1]), sq = split2(q[0], q[1]), sn = split2(nrm[0], nrm[1]);
             rh[i] = sr.hi;
             rl[i] = sr.lo;
             ih[i] = sq.hi;
             il[i] = sq.lo;
+            nh[i] = sn.hi;
+            nl[i] = sn.lo;
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[half], __builtin_bit_cast(bf16x8, rh), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[half], __builtin_bit_cast(bf16x8, rl), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[2 + half], __builtin_bit_cast(bf16x8, ih), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.at[2 + half], __builtin_bit_cast(bf16x8, il), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[0][half], __builtin_bit_cast(bf16x8, nh), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.an[1][half], __builtin_bit_cast(bf16x8, nl), acc, 0, 0, 0);
     }
-    combine_terms(norm_tile16(ka, c, acc), v);
+    combine_terms(acc, v);
 }
 
 // Moments of one head around the stream pivot P: S1 = sum (v - P), S2 = sum (v - P)^2 (fp64),
