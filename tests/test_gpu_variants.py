@@ -254,6 +254,30 @@ def test_offset_max_custom_offsets(orc, T):
     calib.free()
 
 
+@pytest.mark.parametrize("n_off", [17, 18, 19, 32])
+def test_offset_max_many_offsets(orc, T, n_off):
+    """Offset sets of the default size (17), one past it and the largest supported (32): each
+    offset's operands take 4 KB of the block's LDS.  Raw and final scores against the oracle."""
+    import torch
+    G, N = 8, 2500
+    cfg = gc.variant(2, name=f"omax-n{n_off}", n_q_heads=G, n_kv_heads=1, n_seq=1, n_keys=N, budget=800,
+                     t_fixed=N + 3000, seed=393 + n_off)
+    wl = synth.make_host(cfg)
+    dev = synth.to_device(wl)
+    offs = tuple(sorted((i * 7919) % 50000 for i in range(n_off)))     # distinct, 0 among them
+    assert len(set(offs)) == n_off
+    calib = T.load_calib(wl["qc"], wl["qn"], wl["rb"], 1, cfg.theta, offsets=offs)
+    raw = torch.empty((1, 1, G, N), dtype=torch.float32, device="cuda")
+    F = T.score(calib, dev["k"], dev["t_dev"], raw=raw, flags=T.OFFSET_MAX, check=True)
+    torch.cuda.synchronize()
+    res = orc.prune_streams(gc.streams_of(wl["k"], N), gc.streams_of(wl["pos"], N), wl["t"], wl["qc"], wl["qn"],
+                            wl["rb"], cfg.budget, 1, offsets=offs, form="max", want_raw=True)
+    e_raw = gc.check_raw(raw.cpu().numpy().reshape(1, G, N), res["raw"])
+    e_F = gc.check_F(F.cpu().numpy().reshape(1, N), res["F"])
+    print(f"[ok] {n_off} offsets: raw err {e_raw:.2e}  F err {e_F:.2e}", flush=True)
+    calib.free()
+
+
 def test_offset_max_unsupported_cases(T):
     cfg = gc.variant(1, name="omax-f32", n_keys=256, budget=64, seed=392, positions="contiguous", t_fixed=300)
     wl = synth.make_host(cfg)
