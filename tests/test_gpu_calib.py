@@ -67,6 +67,16 @@ def test_calib_stats_qwen3_8b_layer(T, orc):
     assert g_r.min() < 0.5 < g_r.max()        # both diffuse and concentrated heads are covered
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_calib_stats_qwen3_32b_head_count(T, orc, dtype):
+    """Qwen3-32B's 64 layers x 64 query heads: more heads than resident multi-wave blocks, so one
+    wave per head (the launch the calibration bench times), with 43 captured queries (groups of
+    eight rows and a ragged tail of three)."""
+    print(f"\n[case] calib qwen3-32b head count {dtype}", flush=True)
+    q = captured_queries(520, 64, 64, 43, dtype)
+    check(T, orc, q)
+
+
 def test_calib_stats_degenerate_bands(T, orc):
     """A band that is zero in every query has E|q_f| = 0 and R = 0; identical queries give R = 1
     within fp32 rounding."""

@@ -278,6 +278,17 @@ def test_offset_max_many_offsets(orc, T, n_off):
     calib.free()
 
 
+@pytest.mark.parametrize("variant", ["offset_max", "weight_r", "per_key_phase"])
+def test_variants_config5_shape(orc, T, variant):
+    """The variants the bench times, at Qwen3-32B stream shapes (8 KV heads of 8 queries, 32768
+    keys, B = 3072): every stream of one sequence against the oracle, one layer for the maximum over
+    the offsets (its oracle evaluates all 17 offsets per key and head), two for the others."""
+    flags = {"offset_max": T.OFFSET_MAX, "weight_r": T.TRIG_WEIGHT_R, "per_key_phase": T.PER_KEY_PHASE}[variant]
+    cfg = gc.variant(5, name=f"{variant}-c5-shape", n_layers=1 if variant == "offset_max" else 2, n_seq=1,
+                     seed=396)
+    gc.run_case(orc, T, cfg, form="max" if variant == "offset_max" else "fac", flags=flags)
+
+
 def test_offset_max_unsupported_cases(T):
     cfg = gc.variant(1, name="omax-f32", n_keys=256, budget=64, seed=392, positions="contiguous", t_fixed=300)
     wl = synth.make_host(cfg)
