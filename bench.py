@@ -128,26 +128,31 @@ def host_info() -> dict:
     return {"cpu": cpu_model(), "os_cpu_count": os.cpu_count(), "cpus_usable": aff}
 
 
-def copy_bandwidth(torch, dev, nbytes: int = 8 << 30, reps: int = 5) -> float:
+def copy_bandwidth(torch, T, dev, nbytes: int = 8 << 30, reps: int = 5) -> dict:
     """Read + write GB/s of a plain device-to-device copy of nbytes (the best of reps), each rep
-    after a cache flush: the achievable streaming rate the kernels are compared with."""
+    after a cache flush: the achievable streaming rate the kernels are compared with.  "hip": the
+    library's streaming copy kernel (tria_copy, non-temporal 16-byte loads and stores, eight in
+    flight per lane); "torch": torch's copy_."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = float("inf")
-    for _ in range(reps):
-        flush.zero_()
-        torch.cuda.synchronize()
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1))
+    out = {}
+    for name, run in (("hip", lambda: T.copy(src, dst)), ("torch", lambda: dst.copy_(src))):
+        best = float("inf")
+        for _ in range(reps):
+            flush.zero_()
+            torch.cuda.synchronize()
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out[name] = 2 * nbytes / (best * 1e-3) / 1e9
     del src, dst, flush
     torch.cuda.empty_cache()
-    return 2 * nbytes / (best * 1e-3) / 1e9
+    return out
 
 
 def main():
@@ -260,7 +265,8 @@ def main():
         first_ms.append(ev[0].elapsed_time(ev[3]))
     T.score_check(ws)
     restore((k0, v0, pos0), (k, v, pos))
-    copy_gbs = copy_bandwidth(torch, dev)
+    copy_rates = copy_bandwidth(torch, T, dev)
+    copy_gbs = copy_rates["hip"]
 
     step_ms = phase.sum(axis=1)
     ms = float(step_ms.mean())
@@ -321,6 +327,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernels[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name).get(dom)},
         "copy_GB_s": round(copy_gbs, 1),
+        "torch_copy_GB_s": round(copy_rates["torch"], 1),
         "alg_frac_of_copy": round(alg / (ms * 1e-3) / 1e9 / copy_gbs, 4),
         "placement": {"timed_cache": "allocated after the generated pristine copy (K, V, positions)",
                       "ms_per_step_first_allocation": round(float(np.mean(first_ms)), 4),

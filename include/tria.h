@@ -285,6 +285,16 @@ typedef enum {
 tria_status tria_timing_enable(int on);
 tria_status tria_timing_read(double *ms /* [TRIA_TIMER_COUNT] */, int *launches /* [TRIA_TIMER_COUNT] */);
 
+/*
+ * Streaming device copy (instrumentation): copies n_bytes from src to dst, both device buffers
+ * owned by the caller, 16-byte aligned, not overlapping, n_bytes a positive multiple of 16, with
+ * non-temporal 16-byte loads and stores.  It computes nothing of the method: it is the read + write
+ * reference whose rate the benchmark reports beside the prune step's (the in-place compaction reads
+ * and writes every moved row, so a plain copy bounds it).  Asynchronous on stream.  Errors:
+ * INVALID (NULL pointer, zero, ragged or misaligned size, overlapping buffers), DEVICE (launch).
+ */
+tria_status tria_copy(const void *src, void *dst, size_t n_bytes, void *stream);
+
 
 #ifdef __cplusplus
 }

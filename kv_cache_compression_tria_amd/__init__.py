@@ -30,7 +30,7 @@ EXPORTED = (
     "tria_load_calib", "tria_free_calib", "tria_calib_dim", "tria_score_workspace_bytes", "tria_score",
     "tria_score_check", "tria_select_workspace_bytes", "tria_select_topB", "tria_compact",
     "tria_prune_workspace_bytes", "tria_prune", "tria_status_string", "tria_timing_enable", "tria_timing_read",
-    "tria_calib_stats", "tria_append", "tria_decode_step", "tria_prune_static", "tria_band_tables",
+    "tria_calib_stats", "tria_append", "tria_decode_step", "tria_prune_static", "tria_band_tables", "tria_copy",
 )
 TIMERS = ("score_keys", "normalise", "select", "compact", "calib", "select_compact")
 
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.tria_prune_static.argtypes = [P, I, P, P, P, P, I, I, I, P, P, U, ctypes.POINTER(P), P]
         L.tria_timing_read.restype = I
         L.tria_timing_read.argtypes = [ctypes.POINTER(D), ctypes.POINTER(I)]
+        L.tria_copy.restype = I
+        L.tria_copy.argtypes = [P, P, S, P]
         _lib = L
     return _lib
 
@@ -399,6 +401,19 @@ def decode_step(calib: Calib, k, v, pos, t, length: int, budget: int, k_new, v_n
 def timing_enable(on: bool = True):
     """Turn per-kernel event timing on or off (``tria_timing_enable``)."""
     _check(lib().tria_timing_enable(1 if on else 0), "tria_timing_enable")
+
+
+def copy(src, dst, stream=None):
+    """Streaming device copy of src into dst (``tria_copy``; instrumentation: the read + write
+    reference rate).  Both contiguous device tensors of the same byte size, a multiple of 16."""
+    if src is None or dst is None:
+        raise ValueError("copy: src and dst are required")
+    for name, x in (("src", src), ("dst", dst)):
+        _dev(x, name)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("copy: src and dst differ in size")
+    _check(lib().tria_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "tria_copy")
 
 
 def timing_read() -> dict:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtria.so")
-SOURCES = ["abi.cpp", "timing.cpp", "score.hip", "score_mfma.hip", "score_perkey.hip", "calib_stats.hip", "decode.hip", "select.hip", "compact.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "timing.cpp", "score.hip", "score_mfma.hip", "score_perkey.hip", "calib_stats.hip", "decode.hip", "select.hip", "compact.hip", "noalloc.hip", "copy.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

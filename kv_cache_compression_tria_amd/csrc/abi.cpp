@@ -321,6 +321,15 @@ tria_status tria_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const in
     return TRIA_OK;
 }
 
+tria_status tria_copy(const void *src, void *dst, size_t n_bytes, void *stream)
+{
+    if (!src || !dst || n_bytes == 0 || n_bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return TRIA_E_INVALID;
+    const char *s = (const char *)src, *d = (const char *)dst;
+    if (s < d + n_bytes && d < s + n_bytes) return TRIA_E_INVALID;     // the buffers overlap
+    if (tria::launch_copy(src, dst, n_bytes / 16, (hipStream_t)stream) != hipSuccess) return TRIA_E_DEVICE;
+    return TRIA_OK;
+}
+
 size_t tria_prune_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq, int n_keys, int budget,
                                   unsigned flags)
 {

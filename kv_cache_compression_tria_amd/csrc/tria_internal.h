@@ -123,6 +123,8 @@ hipError_t launch_zmax(int G, const float *raw, const double *part, int streams,
 // instead of F; it only places the bracket, so the kept sets do not depend on it.
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard,
                          const float *samp, hipStream_t st);
+// the streaming copy of tria_copy: n16 16-byte words (copy.hip)
+hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
 // selection and compaction in one kernel (tria_prune) for the shapes where select_compact_fused holds

@@ -107,6 +107,19 @@ def test_score_select_compact_validation(tria):
     assert L.tria_prune(None, 0, fake, fake, None, fake, 1, 16, 4, fake, fake, 0, fake, 1 << 20, None) == tria.E_INVALID
 
 
+def test_copy_validation(tria):
+    """tria_copy refuses NULL, empty, ragged, misaligned and overlapping buffers before any launch."""
+    L = tria.lib()
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)     # never dereferenced
+    assert L.tria_copy(None, b, 1024, None) == tria.E_INVALID
+    assert L.tria_copy(a, None, 1024, None) == tria.E_INVALID
+    assert L.tria_copy(a, b, 0, None) == tria.E_INVALID
+    assert L.tria_copy(a, b, 1000, None) == tria.E_INVALID
+    assert L.tria_copy(ctypes.c_void_p(0x100008), b, 1024, None) == tria.E_INVALID
+    assert L.tria_copy(a, ctypes.c_void_p(0x100000 + 512), 1024, None) == tria.E_INVALID
+    assert L.tria_copy(ctypes.c_void_p(0x100000 + 512), a, 1024, None) == tria.E_INVALID
+
+
 def test_timing_api_without_pending_events(tria):
     """Timing can be switched on and off and read with nothing recorded (no GPU needed)."""
     T = tria
