@@ -278,7 +278,7 @@ typedef enum {
     TRIA_TIMER_COMPACT = 3,    /* in-place compaction */
     TRIA_TIMER_CALIB = 4,      /* calibration statistics (tria_calib_stats) */
     TRIA_TIMER_SELECT_COMPACT = 5, /* selection and compaction in one kernel (tria_prune, streams of
-                                      8193 to 32768 keys) */
+                                      up to 32768 keys) */
     TRIA_TIMER_COUNT = 6
 } tria_timer;
 

@@ -12,6 +12,8 @@
 //   select_stream_kernel (streams of 8193 to 32768 keys): brackets T from a sample, passes over F
 //     once, resolves T among the bracketed keys and writes the output from two bitmaps;
 //   select_lds_kernel (streams up to 8192 keys): the same steps over an LDS copy of the keys;
+//   select_compact_kernel, select_lds_compact_kernel (tria_prune): the streamed or the LDS
+//     selection of a stream followed by its compaction, in one block;
 //   select_global_kernel (longer streams): three digits (11, 11, 10 bits) over all keys re-read
 //     from F in every pass; wave w owns the contiguous key range [w*N/16, (w+1)*N/16), and the
 //     candidate list and the output are written in index order from per-wave counts and a prefix
@@ -272,12 +274,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const flo
 // radix digits (11, 11, 10 bits) run over all keys, followed by a bitmap pass.  Finally thread w
 // takes bitmap word w: a block-wide prefix of the words' bit counts places every kept index at
 // slot #(key > T before j) + min(#(key == T before j), k).
+// The selection of stream sid by one block of NT threads (every thread must call it); keys: N
+// words of the block's dynamic LDS.
 template <int NT>
-__global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
-                                                        int32_t *__restrict__ kept, const int *__restrict__ guard)
+__device__ __forceinline__ void select_lds_block(int sid, const float *__restrict__ F, int N, int B,
+                                                 int32_t *__restrict__ kept, const int *__restrict__ guard,
+                                                 uint32_t *keys)
 {
     constexpr int NW = NT / 64;
-    extern __shared__ uint32_t keys[];                // [N]
     __shared__ uint32_t bm[kSelectBitmapWords];       // the two bitmaps, or the fallback's histogram
     __shared__ uint32_t cand[kCand];                  // candidate indices
     __shared__ uint32_t dh[kSelectDigitBins];         // sample histogram, candidate digits
@@ -285,7 +289,6 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
     __shared__ float s_min[NW], s_max[NW];
     __shared__ uint32_t s_prefix, s_k, s_ncand, s_nabove, s_lo, s_hi;
 
-    const int sid = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float *f = F + (size_t)sid * N;
@@ -610,6 +613,14 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict_
         gcarry += tot & 0xffffu;
         ecarry += tot >> 16;
     }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
+                                                        int32_t *__restrict__ kept, const int *__restrict__ guard)
+{
+    extern __shared__ uint32_t keys[];                // [N]
+    select_lds_block<NT>(blockIdx.x, F, N, B, kept, guard, keys);
 }
 
 // Streams up to 32768 keys are selected straight from F (no LDS copy of the keys, 42 KB of LDS, so
@@ -975,25 +986,49 @@ __global__ __launch_bounds__(kSelectCompactThreads) void select_compact_kernel(c
     compact_stream<RV, NT, kSelectCompactRows>(blockIdx.x, k, v, pos, kept, N, B);
 }
 
+// The same for streams that fit the LDS selection (up to kSelectShortKeys keys): the block copies
+// its stream's scores into LDS, selects, and compacts.
+template <int RV>
+__global__ __launch_bounds__(kSelectCompactThreads) void select_lds_compact_kernel(const float *__restrict__ F, int N,
+                                                                                int B, int32_t *__restrict__ kept,
+                                                                                const int *__restrict__ guard,
+                                                                                uint4 *__restrict__ k, uint4 *__restrict__ v,
+                                                                                int32_t *__restrict__ pos)
+{
+    extern __shared__ uint32_t keys[];                // [N]
+    select_lds_block<kSelectCompactThreads>(blockIdx.x, F, N, B, kept, guard, keys);
+    __syncthreads();   // the kept indices written by every thread are visible to the whole block
+    compact_stream<RV, kSelectCompactThreads, kSelectCompactRows>(blockIdx.x, k, v, pos, kept, N, B);
+}
+
 __global__ void identity_kernel(int32_t *__restrict__ kept, int n_streams, int N)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < (size_t)n_streams * N) kept[i] = (int32_t)(i % N);
 }
 
-bool select_compact_fused(int N, int B) { return B < N && N > kSelectShortKeys && N <= kSelectStreamKeys; }
+bool select_compact_fused(int N, int B) { return B < N && N <= kSelectStreamKeys; }
 
 hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, int N, int B, int32_t *kept,
                                  const int *guard, const float *samp, void *k, void *v, int32_t *pos, hipStream_t st)
 {
     if (!select_compact_fused(N, B)) return hipErrorInvalidValue;
     KernelTimer timer(TRIA_TIMER_SELECT_COMPACT, st);
-    if (dt == TRIA_BF16)
+    if (N <= kSelectShortKeys) {
+        const size_t lds = (size_t)N * 4;
+        if (dt == TRIA_BF16)
+            select_lds_compact_kernel<16><<<n_streams, kSelectCompactThreads, lds, st>>>(F, N, B, kept, guard,
+                                                                                       (uint4 *)k, (uint4 *)v, pos);
+        else
+            select_lds_compact_kernel<32><<<n_streams, kSelectCompactThreads, lds, st>>>(F, N, B, kept, guard,
+                                                                                       (uint4 *)k, (uint4 *)v, pos);
+    } else if (dt == TRIA_BF16) {
         select_compact_kernel<16><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, samp,
                                                                              (uint4 *)k, (uint4 *)v, pos);
-    else
+    } else {
         select_compact_kernel<32><<<n_streams, kSelectCompactThreads, 0, st>>>(F, N, B, kept, guard, samp,
                                                                              (uint4 *)k, (uint4 *)v, pos);
+    }
     return hipGetLastError();
 }
 
