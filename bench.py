@@ -8,8 +8,10 @@ in-place compaction of K, V and positions); --entry separate makes the three cal
 Before every step, outside the timed region, K, V and positions are restored from a pristine
 device copy and 1 GiB of scratch is written to evict the 256 MB Infinity Cache and the L2, so
 each step reads a cold, unpruned cache.  Each step is timed with HIP events on the stream the
-kernels run on; the library's own HIP events around each kernel give the per-kernel times and the
-dominant kernel's duration for the roofline.
+kernels run on, enqueued while the restore and flush still run, so that its time is the device's
+(the host's enqueue time of the call is reported apart, host_enqueue_us); the library's own HIP
+events around each kernel give the per-kernel times and the dominant kernel's duration for the
+roofline.
 
 Prints one JSON line (see the keys below).  --gpus above 1 is refused: this path runs on one GPU.
 
@@ -212,12 +214,16 @@ def main():
         if not args.no_flush:
             flush.zero_()
 
+    host_us = []
+
     def step(kk=k, vv=v, pp=pos):
         ev[0].record(stream)
         if args.entry == "prune":
             # the whole step through its own entry point (score, select and compact on one
             # stream); the workspace's error word is checked after the timed loop
+            h0 = time.perf_counter()
             T.prune(calib, kk, vv, pp, t, B, F=F, kept=kept, flags=flags, ws=ws, stream=stream, check=False)
+            host_us.append((time.perf_counter() - h0) * 1e6)
             ev[1].record(stream)
             ev[2].record(stream)
         else:
@@ -235,18 +241,36 @@ def main():
     if args.warmup > 0:
         T.score_check(ws)    # (the workspace's error word is set by the first step)
 
-    # per-kernel HIP-event timing inside the library (events on the stream each kernel runs on)
-    T.timing_read()
-    T.timing_enable(True)
+    # the timed steps (the headline), without the library's per-kernel events
     phase = np.zeros((args.steps, 3))
+    torch.cuda.synchronize()
     wall0 = time.time()
+    host_us.clear()
     for i in range(args.steps):
+        # the restore and the cache flush are still running on the stream while the step is
+        # enqueued behind them, so the step's time is the device's own (the host's enqueue
+        # latency, host_enqueue_us below, is not part of it, as for a caller that enqueues the
+        # step behind other work)
         restore()
-        torch.cuda.synchronize()
         step()
         torch.cuda.synchronize()
         phase[i] = [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])]
     wall_s = time.time() - wall0
+    host_enqueue = list(host_us)
+    T.score_check(ws)
+
+    # The same steps again with per-kernel HIP-event timing inside the library (events on the
+    # stream each kernel runs on): the per-kernel times and the dominant kernel's duration come
+    # from here.  The event records between the kernels lengthen a short step (by ~20 us at
+    # Qwen3-8B batch-1 shapes), so the headline above runs without them.
+    T.timing_read()
+    T.timing_enable(True)
+    inst_ms = []
+    for i in range(args.steps):
+        restore()
+        step()
+        torch.cuda.synchronize()
+        inst_ms.append(ev[0].elapsed_time(ev[3]))
     kern = T.timing_read()
     T.timing_enable(False)
     T.score_check(ws)
@@ -259,7 +283,6 @@ def main():
     first_ms = []
     for i in range(min(args.steps, 5)):
         restore((k0, v0, pos0), (k, v, pos))
-        torch.cuda.synchronize()
         step(k0, v0, pos0)
         torch.cuda.synchronize()
         first_ms.append(ev[0].elapsed_time(ev[3]))
@@ -333,7 +356,9 @@ def main():
                       "ms_per_step_first_allocation": round(float(np.mean(first_ms)), 4),
                       "ms_min_first_allocation": round(float(np.min(first_ms)), 4)},
         "host": host_info(),
+        "ms_per_step_with_kernel_events": round(float(np.mean(inst_ms)), 4),
         "wall_s_timed_loop_incl_restore": round(wall_s, 3),
+        "host_enqueue_us": (round(float(np.mean(host_enqueue)), 1) if host_enqueue else None),
         "gen_s": round(gen_s, 1),
     }
 
@@ -381,19 +406,27 @@ def bench_decode(args, T, torch, synth):
         pn = step()
         T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream, check=False)
     torch.cuda.synchronize()
+
+    def timed(out):
+        for _ in range(args.steps):
+            pn = step()
+            if not args.no_flush:
+                flush.zero_()
+            # enqueued behind the flush: the step's time is the device's own
+            ev[0].record(stream)
+            n = T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream,
+                              check=False)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            assert n == B
+            out.append(ev[0].elapsed_time(ev[1]))
+
+    timed(times)                       # the headline, without the library's per-kernel events
+    T.score_check(ws)
     T.timing_read()
     T.timing_enable(True)
-    for _ in range(args.steps):
-        pn = step()
-        if not args.no_flush:
-            flush.zero_()
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        n = T.decode_step(calib, k, v, pos, t, B, B, kn, vn, pn, F=F, kept=kept, ws=ws, stream=stream, check=False)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        assert n == B
-        times.append(ev[0].elapsed_time(ev[1]))
+    inst = []
+    timed(inst)                        # per-kernel times (events between the kernels)
     kern = T.timing_read()
     T.timing_enable(False)
     T.score_check(ws)
@@ -409,6 +442,7 @@ def bench_decode(args, T, torch, synth):
         "config": {"workload": cfg.name + "-decode-loop", "streams": streams, "capacity": cap, "budget": B,
                    "new_tokens_per_step": n_new, "parallelism": "single-gpu"},
         "generated_tokens_per_s": round(S * n_new / (ms * 1e-3), 1),
+        "ms_per_step_with_kernel_events": round(float(np.mean(inst)), 4),
         "kernels": kernels,
     }
     calib.free()

@@ -151,8 +151,9 @@ tria_status tria_score(const tria_calib *calib, tria_dtype dtype, const void *k,
                        float *head_stats, unsigned flags, void *ws, size_t ws_bytes, void *stream);
 
 /* Synchronise `stream` and report TRIA_E_NONFINITE if the last tria_score on this workspace
- * met a non-finite score, else TRIA_OK (TRIA_E_DEVICE on a runtime error, or when a stream
- * cluster's exchange of partial sums did not complete). */
+ * met a non-finite score, else TRIA_OK (TRIA_E_DEVICE on a runtime error, when a stream
+ * cluster's exchange of partial sums did not complete, or, after tria_prune, when a tile of the
+ * tile-parallel compaction did not see its predecessors hold their rows in time). */
 tria_status tria_score_check(const void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes tria_select_topB needs (0 on bad arguments). */
@@ -177,6 +178,10 @@ tria_status tria_compact(tria_dtype dtype, void *k, void *v, int32_t *pos, const
 
 /* Whole prune step: tria_score, tria_select_topB and tria_compact in sequence on `stream`,
  * with kept written to the caller's buffer.  ws must hold tria_prune_workspace_bytes(..., flags).
+ * With fewer streams than two per compute unit the compaction runs one block per tile of 256
+ * rows instead of one per stream (same results); tria_prune_workspace_bytes then adds 4 bytes
+ * per tile for its synchronisation words (a workspace with room only for tria_score gets the
+ * per-stream compaction).
  * The step is asynchronous, so a scoring failure found on the device (a non-finite score, or a
  * stream cluster's exchange that did not complete) cannot be returned by this call: the selection
  * then writes kept = 0..min(B,N)-1 and K, V and pos are left untouched.  Confirm the step with

@@ -272,7 +272,7 @@ tria_status tria_score_check(const void *ws, size_t ws_bytes, void *stream)
     hipStream_t st = (hipStream_t)stream;
     if (hipMemcpyAsync(&flag, ws, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return TRIA_E_DEVICE;
     if (hipStreamSynchronize(st) != hipSuccess) return TRIA_E_DEVICE;
-    if (flag & 2) return TRIA_E_DEVICE;
+    if (flag & ~1) return TRIA_E_DEVICE;   // a timed-out wait (2: stream cluster, 4: tile compaction)
     return flag ? TRIA_E_NONFINITE : TRIA_OK;
 }
 
@@ -334,7 +334,14 @@ size_t tria_prune_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq,
                                   unsigned flags)
 {
     if (!c || n_seq <= 0 || n_keys <= 0 || budget <= 0) return 0;
-    return tria_score_workspace_bytes(c, dt, n_seq, n_keys, flags);
+    const size_t score = tria_score_workspace_bytes(c, dt, n_seq, n_keys, flags);
+    if (score == 0) return 0;
+    // launches of few streams: the tile-parallel compaction's counter and flags after the score's
+    // workspace
+    const long long n_streams = (long long)n_seq * c->L * c->Hkv;
+    if (n_streams <= 0x7fffffffLL && tria::compact_tiles_applies((int)n_streams, n_keys, budget))
+        return tria::align256(score) + tria::align256(tria::compact_tiles_sync_words((int)n_streams, budget) * 4);
+    return score;
 }
 
 tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int32_t *pos,
@@ -353,6 +360,22 @@ tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int
     const int *guard = (const int *)((const char *)ws + lay.err_off);
     // the stream-cluster scorers leave a side copy of every 16th score, which the selection samples
     const float *samp = lay.cluster ? (const float *)((const char *)ws + lay.samp_off) : nullptr;
+    if (tria::compact_tiles_applies(n_streams, N, B)) {
+        // few streams: selection, then the tile-parallel compaction, when the workspace has room for
+        // its synchronisation words (tria_prune_workspace_bytes reserves them)
+        const size_t sync_off = tria::align256(lay.total);
+        const size_t words = tria::compact_tiles_sync_words(n_streams, B);
+        if (ws_bytes >= sync_off + words * 4) {
+            int *sync = (int *)((char *)ws + sync_off);
+            if (tria::launch_select(F, n_streams, N, B, kept, guard, samp, (hipStream_t)stream, sync,
+                                    tria::compact_tiles_per_stream(B)) != hipSuccess)
+                return TRIA_E_DEVICE;
+            if (tria::launch_compact_tiles(dt, k, v, pos, kept, n_streams, N, B, sync, (int *)guard,
+                                           (hipStream_t)stream) != hipSuccess)
+                return TRIA_E_DEVICE;
+            return TRIA_OK;
+        }
+    }
     if (tria::select_compact_fused(N, B)) {
         // selection and compaction in one kernel (same results as the two calls)
         if (tria::launch_select_compact(dt, F, n_streams, N, B, kept, guard, samp, k, v, pos,

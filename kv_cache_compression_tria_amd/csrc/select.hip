@@ -77,10 +77,23 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Clears the synchronisation words of the tile-parallel compaction that follows the selection in
+// tria_prune (sync: [0] the tile counter, then `words` flags per stream); block sid clears its
+// stream's flags and block 0 the counter.  Plain stores: the compaction is a later launch.
+__device__ __forceinline__ void clear_compact_sync(int *__restrict__ sync, int words, int NT)
+{
+    if (!sync) return;
+    int *w = sync + 1 + (size_t)blockIdx.x * words;
+    for (int i = threadIdx.x; i < words; i += NT) w[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) sync[0] = 0;
+}
+
 __global__ __launch_bounds__(kSelectThreads) void select_global_kernel(const float *__restrict__ F, int N, int B,
                                                                        int32_t *__restrict__ kept,
-                                                                       const int *__restrict__ guard)
+                                                                       const int *__restrict__ guard,
+                                                                       int *__restrict__ sync, int sync_words)
 {
+    clear_compact_sync(sync, sync_words, kSelectThreads);
     constexpr int NT = kSelectThreads;
     constexpr int NW = NT / 64;
     __shared__ uint32_t hist[kBins0];
@@ -617,9 +630,11 @@ __device__ __forceinline__ void select_lds_block(int sid, const float *__restric
 
 template <int NT>
 __global__ __launch_bounds__(NT) void select_lds_kernel(const float *__restrict__ F, int N, int B,
-                                                        int32_t *__restrict__ kept, const int *__restrict__ guard)
+                                                        int32_t *__restrict__ kept, const int *__restrict__ guard,
+                                                        int *__restrict__ sync, int sync_words)
 {
     extern __shared__ uint32_t keys[];                // [N]
+    clear_compact_sync(sync, sync_words, NT);
     select_lds_block<NT>(blockIdx.x, F, N, B, kept, guard, keys);
 }
 
@@ -960,8 +975,10 @@ __device__ __forceinline__ void select_stream_block(int sid, const float *__rest
 template <int NT, int SMAX, int DEPTH>
 __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ F, int N, int B,
                                                            int32_t *__restrict__ kept, const int *__restrict__ guard,
-                                                           const float *__restrict__ samp)
+                                                           const float *__restrict__ samp, int *__restrict__ sync,
+                                                           int sync_words)
 {
+    clear_compact_sync(sync, sync_words, NT);
     select_stream_block<NT, SMAX, DEPTH>(blockIdx.x, F, N, B, kept, guard, samp);
 }
 
@@ -1033,7 +1050,7 @@ hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, i
 }
 
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard,
-                         const float *samp, hipStream_t st)
+                         const float *samp, hipStream_t st, int *sync, int sync_words)
 {
     KernelTimer timer(TRIA_TIMER_SELECT, st);
     if (B >= N) {
@@ -1042,11 +1059,12 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
         return hipGetLastError();
     }
     if (N <= kSelectShortKeys) {
-        select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept, guard);
+        select_lds_kernel<256><<<n_streams, 256, (size_t)N * 4, st>>>(F, N, B, kept, guard, sync, sync_words);
     } else if (N <= kSelectStreamKeys) {
-        select_stream_kernel<512, kSelectSamples, 4><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard, samp);
+        select_stream_kernel<512, kSelectSamples, 4><<<n_streams, 512, 0, st>>>(F, N, B, kept, guard, samp, sync,
+                                                                                 sync_words);
     } else {
-        select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept, guard);
+        select_global_kernel<<<n_streams, kSelectThreads, 0, st>>>(F, N, B, kept, guard, sync, sync_words);
     }
     return hipGetLastError();
 }

@@ -54,6 +54,7 @@ constexpr int kSampleStride = 16;     // the cluster scorers copy every 16th key
 constexpr int kCompactThreads = 1024;   // the compaction kernel: one block of 16 waves per stream,
 constexpr int kCompactRows = 256;       // 256 rows per tile (few streams move faster with wide blocks)
 constexpr int kSelectCompactRows = 128; // rows per tile of the fused selection + compaction (1024 threads)
+constexpr int kTileCompactRows = 256;   // rows per block of the tile-parallel compaction (1024 threads)
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -121,12 +122,24 @@ hipError_t launch_zmax(int G, const float *raw, const double *part, int streams,
 // place) instead of selecting.  samp (device, may be null): the cluster scorers' side copy of every
 // kSampleStride-th score ([streams][ceil(N / kSampleStride)]), which the streamed selection samples
 // instead of F; it only places the bracket, so the kept sets do not depend on it.
+// sync (device, may be null): the tile-parallel compaction's counter and flags (sync_words flags per
+// stream), which the selection clears for the compaction launched after it
 hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *kept, const int *guard,
-                         const float *samp, hipStream_t st);
+                         const float *samp, hipStream_t st, int *sync = nullptr, int sync_words = 0);
 // the streaming copy of tria_copy: n16 16-byte words (copy.hip)
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
+// The tile-parallel compaction (tria_prune, launches of few streams): one block per tile of
+// kTileCompactRows destination rows.  compact_tiles_applies: whether tria_prune takes it for
+// n_streams streams on the current device; compact_tiles_sync_words: its counter and flags (ints,
+// to be cleared by the selection launched before it, see launch_select); err: the step's error
+// word (bit 4 set if a tile's wait for its predecessors timed out).
+bool compact_tiles_applies(int n_streams, int N, int B);
+size_t compact_tiles_sync_words(int n_streams, int B);
+int compact_tiles_per_stream(int B);
+hipError_t launch_compact_tiles(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept, int n_streams,
+                                int N, int B, int *sync, int *err, hipStream_t st);
 // selection and compaction in one kernel (tria_prune) for the shapes where select_compact_fused holds
 bool select_compact_fused(int N, int B);
 hipError_t launch_select_compact(tria_dtype dt, const float *F, int n_streams, int N, int B, int32_t *kept,
