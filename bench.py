@@ -16,8 +16,9 @@ roofline.
 Prints one JSON line (see the keys below).  --gpus above 1 is refused: this path runs on one GPU.
 
 --workload decode measures the decode loop on config 4 (Qwen3-8B shapes, 36 layers x 64
-sequences x 8 KV heads, B = 2048): one step appends the K/V rows of 128 new tokens to every
-stream and prunes the full cache (B + 128 rows) back to B (tria_decode_step).
+sequences x 8 KV heads, B = 2048; --config 3: one sequence, B = 3072): one step appends the K/V
+rows of 128 new tokens to every stream and prunes the full cache (B + 128 rows) back to B
+(tria_decode_step).
 
 --workload calib measures instead the calibration-statistics kernel (tria_calib_stats) on the
 offline capture it would see for Qwen3-32B: 64 layers x 64 query heads x 10240 captured pre-RoPE
@@ -81,7 +82,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=5, help="workload id (1..5), see synth.py")
+    ap.add_argument("--config", type=int, default=None,
+                    help="workload id (1..5), see synth.py; default 5 (prune), 4 (decode: 3 or 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
@@ -177,6 +179,8 @@ def main():
         return bench_calib(args, T, torch)
     if args.workload == "decode":
         return bench_decode(args, T, torch, synth)
+    if args.config is None:
+        args.config = 5
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -371,10 +375,16 @@ def main():
 
 
 def bench_decode(args, T, torch, synth):
-    """Decode loop on config 4 shapes: append 128 tokens' rows, prune B + 128 -> B, per step."""
-    cfg = synth.CONFIGS[4]
+    """Decode loop on config 4 shapes (Qwen3-8B, batch 64), or with --config 3 on Qwen3-8B batch-1
+    shapes: append 128 tokens' rows, prune B + 128 -> B, per step."""
+    cid = 4 if args.config is None else args.config
+    if cid not in (3, 4):
+        sys.exit(f"bench.py: the decode loop runs on config 3 or 4 (a cache of B + 128 keys), not {cid}")
+    cfg = synth.CONFIGS[cid]
     dev = torch.device("cuda:0")
-    wl = synth.make_device(cfg, dev)             # N = B + 128 keys: a full cache
+    # N = B + 128 keys: a full cache
+    wl = synth.make_device(cfg, dev) if cid >= 4 else synth.to_device(synth.make_host(cfg), dev)
+    assert cfg.n_keys == cfg.budget + 128
     k, v, pos, t = wl["k"], wl["v"], wl["pos"], wl["t_dev"].clone()
     S, L, Hkv, cap, d = k.shape
     B = cfg.budget
