@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--workload", choices=("prune", "decode", "calib"), default="prune",
                     help="prune: the prune step (default); decode: append 128 tokens + prune per step; "
                          "calib: calibration statistics of captured queries")
+    ap.add_argument("--graph", action="store_true",
+                    help="prune workload: time replays of the step captured once in a HIP graph")
     ap.add_argument("--entry", choices=("prune", "separate"), default="prune",
                     help="prune: one tria_prune call per step (default); separate: tria_score, "
                          "tria_select_topB and tria_compact")
@@ -219,10 +221,17 @@ def main():
             flush.zero_()
 
     host_us = []
+    graph = None                      # --graph: the step on (k, v, pos) captured once
 
-    def step(kk=k, vv=v, pp=pos):
+    def step(kk=k, vv=v, pp=pos, replay=False):
         ev[0].record(stream)
-        if args.entry == "prune":
+        if replay:
+            h0 = time.perf_counter()
+            graph.replay()
+            host_us.append((time.perf_counter() - h0) * 1e6)
+            ev[1].record(stream)
+            ev[2].record(stream)
+        elif args.entry == "prune":
             # the whole step through its own entry point (score, select and compact on one
             # stream); the workspace's error word is checked after the timed loop
             h0 = time.perf_counter()
@@ -244,6 +253,14 @@ def main():
     torch.cuda.synchronize()
     if args.warmup > 0:
         T.score_check(ws)    # (the workspace's error word is set by the first step)
+    if args.graph:
+        if args.entry != "prune":
+            sys.exit("bench.py: --graph captures the tria_prune step (--entry prune)")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            # the capture stream is the current one inside the context; nothing runs until replay
+            T.prune(calib, k, v, pos, t, B, F=F, kept=kept, flags=flags, ws=ws, check=False)
+        torch.cuda.synchronize()
 
     # the timed steps (the headline), without the library's per-kernel events
     phase = np.zeros((args.steps, 3))
@@ -256,7 +273,7 @@ def main():
         # latency, host_enqueue_us below, is not part of it, as for a caller that enqueues the
         # step behind other work)
         restore()
-        step()
+        step(replay=graph is not None)
         torch.cuda.synchronize()
         phase[i] = [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])]
     wall_s = time.time() - wall0
@@ -342,7 +359,8 @@ def main():
         "config": {"workload": cfg.name, "streams": n_streams, "keys_per_stream": N, "budget": B,
                    "layers": L, "seqs": S, "q_heads": cfg.n_q_heads, "kv_heads": Hkv, "head_dim": d,
                    "cache_dtype": cfg.dtype, "score_variant": args.variant, "score_path": args.score_path,
-                   "entry": "tria_prune" if args.entry == "prune" else "tria_score+tria_select_topB+tria_compact", "parallelism": "single-gpu"},
+                   "entry": "tria_prune" if args.entry == "prune" else "tria_score+tria_select_topB+tria_compact",
+                   "hip_graph": graph is not None, "parallelism": "single-gpu"},
         "alg_bytes_per_step": int(alg),
         "alg_GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
