@@ -129,3 +129,23 @@ def test_score_sized_workspace_takes_the_per_stream_compaction(T):
     assert torch.equal(F1, F2) and torch.equal(kept1, kept2)
     _same(torch, ref, d)
     calib.free()
+
+
+@pytest.mark.parametrize("word,status", [(0, "OK"), (1, "E_NONFINITE"), (2, "E_DEVICE"), (4, "E_DEVICE"),
+                                         (5, "E_DEVICE")])
+def test_score_check_reads_every_error_bit(T, word, status):
+    """The step's error word (the workspace's first int): bit 0 a non-finite score, bit 1 a stream
+    cluster's exchange that did not complete, bit 2 a tile of the tile-parallel compaction whose
+    wait ran past its bound.  tria_score_check reports the first as TRIA_E_NONFINITE and the
+    others as TRIA_E_DEVICE (set here from the host; no kernel is made to fail)."""
+    import torch
+    ws = T.workspace(256)
+    ws.zero_()
+    ws[:4].copy_(torch.tensor([word], dtype=torch.int32).view(torch.uint8))
+    torch.cuda.synchronize()
+    if status == "OK":
+        T.score_check(ws)
+        return
+    with pytest.raises(T.TriaError) as e:
+        T.score_check(ws)
+    assert e.value.status == getattr(T, status)
