@@ -149,3 +149,20 @@ def test_score_check_reads_every_error_bit(T, word, status):
     with pytest.raises(T.TriaError) as e:
         T.score_check(ws)
     assert e.value.status == getattr(T, status)
+
+
+def test_tile_compaction_without_positions(T):
+    """No positions array (pos = NULL): K and V move as with the per-stream compaction."""
+    import torch
+    print("\n[case] tile compaction without positions", flush=True)
+    cfg, wl, calib = _case(T, "bf16", 4, 3200, 3072, n_seq=1, n_layers=2, seed=73)
+    d1, d2 = synth.to_device(wl), synth.to_device(wl)
+    F1 = T.score(calib, d1["k"], d1["t_dev"], check=True)
+    kept1 = T.select_topB(F1, cfg.budget)
+    T.compact(d1["k"], d1["v"], None, kept1, cfg.budget)
+    F2, kept2 = T.prune(calib, d2["k"], d2["v"], None, d2["t_dev"], cfg.budget)
+    torch.cuda.synchronize()
+    assert torch.equal(F1, F2) and torch.equal(kept1, kept2)
+    assert torch.equal(d1["k"].view(torch.int16), d2["k"].view(torch.int16))
+    assert torch.equal(d1["v"].view(torch.int16), d2["v"].view(torch.int16))
+    calib.free()
