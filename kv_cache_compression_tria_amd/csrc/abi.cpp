@@ -336,8 +336,7 @@ size_t tria_prune_workspace_bytes(const tria_calib *c, tria_dtype dt, int n_seq,
     if (!c || n_seq <= 0 || n_keys <= 0 || budget <= 0) return 0;
     const size_t score = tria_score_workspace_bytes(c, dt, n_seq, n_keys, flags);
     if (score == 0) return 0;
-    // launches of few streams: the tile-parallel compaction's counter and flags after the score's
-    // workspace
+    // the tile-parallel compaction's counter and flags after the score's workspace
     const long long n_streams = (long long)n_seq * c->L * c->Hkv;
     if (n_streams <= 0x7fffffffLL && tria::compact_tiles_applies((int)n_streams, n_keys, budget))
         return tria::align256(score) + tria::align256(tria::compact_tiles_sync_words((int)n_streams, budget) * 4);
@@ -361,8 +360,9 @@ tria_status tria_prune(const tria_calib *c, tria_dtype dt, void *k, void *v, int
     // the stream-cluster scorers leave a side copy of every 16th score, which the selection samples
     const float *samp = lay.cluster ? (const float *)((const char *)ws + lay.samp_off) : nullptr;
     if (tria::compact_tiles_applies(n_streams, N, B)) {
-        // few streams: selection, then the tile-parallel compaction, when the workspace has room for
-        // its synchronisation words (tria_prune_workspace_bytes reserves them)
+        // the selection, then the tile-parallel compaction, when the workspace has room for its
+        // synchronisation words (tria_prune_workspace_bytes reserves them); else the fused
+        // per-stream selection and compaction below
         const size_t sync_off = tria::align256(lay.total);
         const size_t words = tria::compact_tiles_sync_words(n_streams, B);
         if (ws_bytes >= sync_off + words * 4) {

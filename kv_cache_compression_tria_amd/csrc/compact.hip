@@ -1,6 +1,6 @@
 // compact.hip -- in-place, order-preserving compaction of K, V and positions (gfx950): one block
 // per stream (the method and its ordering argument are in compact_stream.cuh), and the
-// tile-parallel form that tria_prune takes for launches of few streams.
+// tile-parallel form that tria_prune takes.
 #include <mutex>
 
 #include "compact_stream.cuh"
@@ -30,7 +30,8 @@ hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const i
 
 // The tile-parallel compaction: one block of kCompactThreads per tile of T destination rows, the
 // tiles of every stream in flight at once (one block per stream leaves CUs idle when there are
-// about as many streams as CUs, and one CU moves a stream at a small fraction of the chip's rate).
+// about as many streams as CUs, and one CU moves a stream at a small fraction of the chip's rate;
+// with many streams the tiles still keep more rows in flight than sequential per-stream passes).
 //
 // Tile q of a stream writes rows [qT, qT + T) and reads rows kept[i] >= i of the same index range
 // (chenxutan.com/d/2624 section 4.2: the cache is indexed by the sorted kept indices).  Its
@@ -152,13 +153,16 @@ int device_cus()
 
 int compact_tiles_per_stream(int B) { return (B + kTileCompactRows - 1) / kTileCompactRows; }
 
-// Fewer streams than two per compute unit: one block per stream would leave the chip short of work.
+// Every launch with rows to move and a grid that fits.  Measured on MI355X against one fused
+// selection-and-compaction block per stream: with few streams one block per stream leaves CUs idle
+// (Qwen3-8B batch 1: 0.231 -> 0.021 + 0.166 ms), and with many the tiles still move rows faster than
+// the per-stream passes do even with the selection as a launch of its own (Qwen3-8B batch 64: 7.42
+// -> 0.38 + 6.43 ms; Qwen3-32B: 2.62-2.71 -> 0.23 + 2.20-2.22 ms).
 bool compact_tiles_applies(int n_streams, int N, int B)
 {
     if (B >= N || n_streams <= 0) return false;
     if ((long long)n_streams * compact_tiles_per_stream(B) > 0x7fffffffLL) return false;
-    const int cus = device_cus();
-    return cus > 0 && n_streams < 2 * cus;
+    return device_cus() > 0;
 }
 
 size_t compact_tiles_sync_words(int n_streams, int B) { return 1 + (size_t)n_streams * compact_tiles_per_stream(B); }

@@ -130,9 +130,9 @@ hipError_t launch_select(const float *F, int n_streams, int N, int B, int32_t *k
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
-// The tile-parallel compaction (tria_prune, launches of few streams): one block per tile of
-// kTileCompactRows destination rows.  compact_tiles_applies: whether tria_prune takes it for
-// n_streams streams on the current device; compact_tiles_sync_words: its counter and flags (ints,
+// The tile-parallel compaction (tria_prune): one block per tile of kTileCompactRows destination
+// rows.  compact_tiles_applies: whether tria_prune takes it for n_streams streams on the current
+// device (every launch with rows to move); compact_tiles_sync_words: its counter and flags (ints,
 // to be cleared by the selection launched before it, see launch_select); err: the step's error
 // word (bit 4 set if a tile's wait for its predecessors timed out).
 bool compact_tiles_applies(int n_streams, int N, int B);

@@ -1,5 +1,6 @@
-"""GPU: the tile-parallel compaction that tria_prune takes for launches of fewer streams than two
-per compute unit (one block per tile of 256 destination rows, every tile of every stream in flight).
+"""GPU: the tile-parallel compaction that tria_prune takes (one block per tile of 256 destination
+rows, every tile of every stream in flight), and its fallback when the workspace has no room for its
+synchronisation words.
 
 Each case compares tria_prune (score, selection, tile-parallel compaction) with the three separate
 calls (score, selection, the per-stream compaction of tria_compact) on the same seeded cache, bit
