@@ -178,9 +178,11 @@ tria_status tria_compact(tria_dtype dtype, void *k, void *v, int32_t *pos, const
 
 /* Whole prune step: tria_score, tria_select_topB and tria_compact in sequence on `stream`,
  * with kept written to the caller's buffer.  ws must hold tria_prune_workspace_bytes(..., flags).
- * The compaction runs one block per tile of 256 rows (same results as tria_compact's one block per
- * stream); tria_prune_workspace_bytes adds 4 bytes per tile for its synchronisation words (a
- * workspace with room only for tria_score gets a fused per-stream selection and compaction).
+ * With fewer streams than two per compute unit, or streams of at most 8192 keys, the compaction
+ * runs one block per tile of 256 rows (same results as tria_compact's one block per stream);
+ * tria_prune_workspace_bytes then adds 4 bytes per tile for its synchronisation words (a workspace
+ * with room only for tria_score gets a fused per-stream selection and compaction, as do many
+ * longer streams).
  * The step is asynchronous, so a scoring failure found on the device (a non-finite score, or a
  * stream cluster's exchange that did not complete) cannot be returned by this call: the selection
  * then writes kept = 0..min(B,N)-1 and K, V and pos are left untouched.  Confirm the step with

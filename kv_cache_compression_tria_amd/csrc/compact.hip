@@ -153,16 +153,18 @@ int device_cus()
 
 int compact_tiles_per_stream(int B) { return (B + kTileCompactRows - 1) / kTileCompactRows; }
 
-// Every launch with rows to move and a grid that fits.  Measured on MI355X against one fused
-// selection-and-compaction block per stream: with few streams one block per stream leaves CUs idle
-// (Qwen3-8B batch 1: 0.231 -> 0.021 + 0.166 ms), and with many the tiles still move rows faster than
-// the per-stream passes do even with the selection as a launch of its own (Qwen3-8B batch 64: 7.42
-// -> 0.38 + 6.43 ms; Qwen3-32B: 2.62-2.71 -> 0.23 + 2.20-2.22 ms).
+// Measured on MI355X against one fused selection-and-compaction block per stream, in the same
+// process on the same cache: with fewer streams than two per CU one block per stream leaves CUs
+// idle (Qwen3-8B batch 1: 0.231 -> 0.021 + 0.166 ms); with many streams of up to 8192 keys the tiles
+// still move rows faster than the per-stream passes even with the selection as a launch of its own
+// (Qwen3-8B batch 64: 7.42 -> 0.39 + 6.43 ms); with many long streams the fused kernel, whose
+// selection hides behind other blocks' rows, stays ahead (Qwen3-32B: 2.63 against 0.25 + 2.43 ms).
 bool compact_tiles_applies(int n_streams, int N, int B)
 {
     if (B >= N || n_streams <= 0) return false;
     if ((long long)n_streams * compact_tiles_per_stream(B) > 0x7fffffffLL) return false;
-    return device_cus() > 0;
+    const int cus = device_cus();
+    return cus > 0 && (n_streams < 2 * cus || N <= kTileCompactShortKeys);
 }
 
 size_t compact_tiles_sync_words(int n_streams, int B) { return 1 + (size_t)n_streams * compact_tiles_per_stream(B); }

@@ -55,6 +55,7 @@ constexpr int kCompactThreads = 1024;   // the compaction kernel: one block of 1
 constexpr int kCompactRows = 256;       // 256 rows per tile (few streams move faster with wide blocks)
 constexpr int kSelectCompactRows = 128; // rows per tile of the fused selection + compaction (1024 threads)
 constexpr int kTileCompactRows = 256;   // rows per block of the tile-parallel compaction (1024 threads)
+constexpr int kTileCompactShortKeys = 8192;  // with many streams, the tile compaction for streams up to this long
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -131,8 +132,8 @@ hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t st);
 hipError_t launch_compact(tria_dtype dt, void *k, void *v, int32_t *pos, const int32_t *kept,
                           int n_streams, int N, int B, hipStream_t st);
 // The tile-parallel compaction (tria_prune): one block per tile of kTileCompactRows destination
-// rows.  compact_tiles_applies: whether tria_prune takes it for n_streams streams on the current
-// device (every launch with rows to move); compact_tiles_sync_words: its counter and flags (ints,
+// rows.  compact_tiles_applies: whether tria_prune takes it for n_streams streams of N keys on the
+// current device (fewer streams than two per CU, or streams of up to kTileCompactShortKeys keys); compact_tiles_sync_words: its counter and flags (ints,
 // to be cleared by the selection launched before it, see launch_select); err: the step's error
 // word (bit 4 set if a tile's wait for its predecessors timed out).
 bool compact_tiles_applies(int n_streams, int N, int B);
